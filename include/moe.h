@@ -1,0 +1,181 @@
+/*
+ * moe.h — C ABI of the routed mixture-of-experts layer for AMD MI355X (gfx950).
+ *
+ * The layer runs an LLM's routed MoE block directly on checkpoint-format
+ * quantized expert weights: NVFP4, MXFP4 and FP8 E4M3 with 128x128 block
+ * scales, BF16 activations, FP32 accumulation, no dequantized weight copy.
+ * Serving checkpoints as published, with kernels written per weight format and
+ * no conversion step, is the premise of the DGPP pages ("DGPP" README, intro
+ * bullet on checkpoint formats; forum thread "DGPP: a GB10-optimized C++/CUDA
+ * inference engine", opening post, quantization table).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named *in the descriptor and in the calls* are DEVICE pointers,
+ *   owned by the caller; the library never allocates, frees or keeps them.
+ *   The descriptor structs themselves are read on the host during the call.
+ * - All work is queued on `stream` (a hipStream_t; NULL = the default
+ *   stream).  No entry point synchronises the stream, so every call may be
+ *   captured into a HIP graph.
+ * - Argument and shape checks run on the host before anything is queued and
+ *   return a negative MOE_ERR_* code; nothing is launched then.  A failed
+ *   launch returns MOE_ERR_HIP.  Faults inside kernels surface at the
+ *   caller's next synchronisation.
+ * - No silent fallback: an unsupported shape or format returns
+ *   MOE_ERR_UNSUPPORTED; there is no slow path.
+ * - T = 0 is a no-op returning MOE_OK.
+ * - bf16 values are passed as uint16_t bit patterns.
+ * - Results are deterministic: the same inputs give bit-identical outputs run
+ *   after run (no floating-point atomics; fixed reduction orders).  The pages
+ *   hold the serving chain to the same contract ("DGPP" README, the paragraph
+ *   on the default chain being exact and repeatable).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer, bad size, bad descriptor */
+#define MOE_ERR_UNSUPPORTED (-2) /* valid request this library does not run */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
+#define MOE_ERR_HIP (-4)         /* a HIP launch failed */
+
+/* ---- weight formats (one projection of E stacked experts) --------------- */
+/* NVFP4: codes uint8 [E][rows][cols/2], two E2M1 codes per byte with the
+ *   even K index in the low nibble; scales uint8 E4M3 [E][rows][cols/16]
+ *   (one per 16 consecutive K of a row); tensor_scale fp32 [E].
+ *   W[n,k] = e2m1(q[n,k]) * e4m3(S[n,k/16]) * tensor_scale[e].
+ *   Requires cols % 32 == 0.
+ * MXFP4: codes as NVFP4; scales uint8 E8M0 [E][rows][cols/32];
+ *   tensor_scale NULL.  W[n,k] = e2m1(q[n,k]) * 2^(S[n,k/32]-127).
+ *   Requires cols % 32 == 0.
+ * FP8_B128: codes uint8 E4M3 ("fn") [E][rows][cols]; scales fp32
+ *   [E][ceil(rows/128)][ceil(cols/128)]; tensor_scale NULL.
+ *   W[n,k] = e4m3(Q[n,k]) * S[n/128][k/128].  Requires cols % 16 == 0.
+ * Element and scale encodings are those of the OCP Microscaling Formats v1.0
+ * (E2M1, E8M0) and OCP 8-bit Floating Point (E4M3) specifications.         */
+#define MOE_FMT_NVFP4 1
+#define MOE_FMT_MXFP4 2
+#define MOE_FMT_FP8_B128 3
+
+typedef struct moe_qweight {
+  int32_t format;      /* MOE_FMT_* */
+  int32_t rows;        /* output features (logical [rows][cols], K = cols contiguous) */
+  int32_t cols;        /* input features (the contraction dimension) */
+  int32_t num_experts; /* E stacked experts */
+  const uint8_t* codes;
+  const void* scales;
+  const float* tensor_scale;    /* NVFP4 only, else NULL */
+  int64_t expert_stride_codes;  /* bytes between experts in `codes`, 16-byte multiple */
+  int64_t expert_stride_scales; /* bytes between experts in `scales` */
+} moe_qweight;
+
+/* One layer.  Router weight fp32 [H][E] row-major; optional fp32 [E]
+ * per-expert logit offsets.  Routed projections: gate and up [E][I][H],
+ * down [E][H][I].  Optional always-on shared expert (weight 1): sh_gate,
+ * sh_up [1][I_shared][H], sh_down [1][H][I_shared].                        */
+typedef struct moe_layer_desc {
+  int32_t H, I, E, top_k;
+  int32_t renormalize; /* 1: softmax over the k selected logits; 0: full softmax gathered */
+  const float* router_w;
+  const float* router_bias;
+  moe_qweight gate, up, down;
+  int32_t has_shared, I_shared;
+  moe_qweight sh_gate, sh_up, sh_down;
+} moe_layer_desc;
+
+/* ---- expert-GEMM operations ---------------------------------------------- */
+#define MOE_OP_GATE_UP_SWIGLU 0 /* in bf16 [rows][H] -> h bf16 [rows][I]: h = bf16(silu(x.Wg^T)*(x.Wu^T)) */
+#define MOE_OP_DOWN 1           /* in bf16 [rows][I] -> y fp32 [rows][H]: y = h.Wd^T */
+
+int32_t moe_abi_version(void);
+const char* moe_status_string(int32_t status);
+
+/* Text of the last HIP error this library saw on the calling thread (after a
+ * MOE_ERR_HIP), or "" if none.  The string is owned by the library. */
+const char* moe_last_error(void);
+
+/* Host-only check of a layer descriptor (no HIP call): MOE_OK or a negative code. */
+int32_t moe_validate_layer(const moe_layer_desc* L);
+
+/* Workspace bytes every entry point below needs for this layer and T tokens.
+ * A workspace of at least this size (256-byte aligned device memory) serves
+ * any call with the same (L, T); it needs no initialisation.  Returns 0 when
+ * the descriptor is invalid. */
+size_t moe_workspace_size(const moe_layer_desc* L, int32_t T);
+
+/* Router softmax + top-k (the router function, top-k and tie rule are not on
+ * the pages; this follows a softmax router with k largest logits, ties to the
+ * lower expert id, outputs in descending logit order).
+ *   x        bf16 [T][H] or NULL.
+ *   logits   fp32 [T][E].  If x is NULL: input, and routing is decided on
+ *            these values exactly.  Else: output, l = x.Wr + b rounded to fp32;
+ *            routing is then decided on the exact logits rounded once to
+ *            float64 (a rigorous error bound certifies the fast sum; uncertain
+ *            tokens are recomputed with a compensated float64 sum).
+ *   topk_ids int32 [T][k]; topk_w fp32 [T][k] (softmax over the k selected,
+ *            or over all E when renormalize == 0).
+ * NaN logits rank after every number. */
+int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits, int32_t T,
+                       int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Grouping of the T*k (token, slot) pairs by expert: a stable counting sort
+ * (pairs in t-major, slot order within each expert).
+ *   topk_ids int32 [T][k] with values in [0, E) (other values: undefined).
+ *   counts [E]; offsets [E+1] (exclusive scan of counts);
+ *   perm_to_pair [T*k]: permuted row -> pair t*k+j; pair_to_perm [T*k]: inverse.
+ * Workspace: moe_permute_workspace_size(T, k, E) bytes. */
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
+int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                    int32_t* offsets, int32_t* perm_to_pair, int32_t* pair_to_perm, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* One expert projection pass over grouped rows.
+ *   shared = 0: routed experts; rows are the T*k permuted pairs grouped by
+ *     `offsets` [E+1]; for op GATE_UP the input row of permuted row p is
+ *     token perm_to_pair[p]/k of `in` (x bf16 [T][H]); for op DOWN the input
+ *     row is p of `in` (h bf16 [T*k][I]).  Output row p in permuted order.
+ *   shared = 1: the shared expert over T rows of `in`; offsets/perm_to_pair unused.
+ *   out: GATE_UP -> bf16 [rows][I or I_shared]; DOWN -> fp32 [rows][H].
+ * Accumulation is fp32; products of the decoded weight and the bf16 input are
+ * exact.  The intermediate h is BF16 (activations stay BF16, forum opening
+ * post).  The kernel variant follows the row count (row-aware lowering, gitee
+ * "dgpp" README, "Highlights"): groups of up to 16 rows stream weights once
+ * per group, larger groups run as tiled grouped GEMM. */
+int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
+                        const int32_t* offsets, const int32_t* perm_to_pair, int32_t T,
+                        const uint16_t* in, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine (partials kept in fp32, summed in slot order; bf16
+ * partials are a lossy lever on the pages, gitee "dgpp" README, "Execution
+ * and performance", engine.prefill_bf16_partials):
+ *   out[t] = bf16( sum_{j<k} w[t,j] * y_perm[pair_to_perm[t*k+j]] + y_shared[t] ).
+ *   y_perm fp32 [T*k][H]; topk_w fp32 [T][k]; y_shared fp32 [T][H] or NULL;
+ *   out bf16 [T][H]. */
+int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pair_to_perm,
+                    const float* y_shared, int32_t T, int32_t k, int32_t H, uint16_t* out,
+                    void* stream);
+
+/* The whole layer: route, group, gate/up + SwiGLU, down, shared expert,
+ * combine.  x bf16 [T][H] -> out bf16 [T][H].  Optional debug outputs
+ * (NULL to skip): logits fp32 [T][E], ids int32 [T][k], weights fp32 [T][k].
+ * T <= 8 runs the decode lowering (weights streamed once per active expert);
+ * larger T the prefill lowering (grouped GEMM over a tile list). */
+int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
+                          void* ws, size_t ws_bytes, float* dbg_logits, int32_t* dbg_ids,
+                          float* dbg_w, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

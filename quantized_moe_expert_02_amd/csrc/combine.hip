@@ -1,0 +1,43 @@
+// Weighted combine of the per-expert partials.
+//
+// The default chain keeps expert partial sums in fp32; summing them from bf16
+// is an explicit lossy lever (gitee "dgpp" README, "Execution and
+// performance", engine.prefill_bf16_partials).  Each output element sums its
+// k partials in slot order, then the shared expert, then rounds once to bf16:
+// a fixed order, so the result does not depend on scheduling.
+#include "moe_launch.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const float* __restrict__ w,
+                                                      const int* __restrict__ p2p,
+                                                      const float* __restrict__ ys, int T, int k,
+                                                      int H, uint16_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= H) return;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int pp = p2p[(size_t)t * k + j];
+    const float wj = w[(size_t)t * k + j];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(y + (size_t)pp * H + n);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+  }
+  if (ys != nullptr) acc = acc + *reinterpret_cast<const f32x4*>(ys + (size_t)t * H + n);
+  const uint2 o = make_uint2(f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16),
+                             f32_to_bf16(acc[2]) | (uint32_t(f32_to_bf16(acc[3])) << 16));
+  *reinterpret_cast<uint2*>(out + (size_t)t * H + n) = o;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y, const float* w, const int* pair_to_perm, const float* ys,
+                          int T, int k, int H, uint16_t* out, hipStream_t s) {
+  dim3 grid((H / 4 + 255) / 256, T);
+  return launch(combine_kernel, grid, dim3(256), 0, s, y, w, pair_to_perm, ys, T, k, H, out);
+}
+
+}  // namespace moe

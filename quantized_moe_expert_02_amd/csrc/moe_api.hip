@@ -1,0 +1,361 @@
+// The C ABI: host-side validation, workspace planning and launch sequencing.
+//
+// Bad configuration is rejected before anything runs and never falls back
+// silently (gitee "dgpp" README, "Configuration": unknown keys and invalid
+// types are rejected; the startup memory plan is checked before allocation).
+// Here that means: every descriptor and size is checked on the host, a
+// negative status comes back before any launch, and the caller sizes the
+// workspace from moe_workspace_size() up front.
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "moe_launch.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int fmt_of(int32_t f) {
+  switch (f) {
+    case MOE_FMT_NVFP4: return FMT_NVFP4;
+    case MOE_FMT_MXFP4: return FMT_MXFP4;
+    case MOE_FMT_FP8_B128: return FMT_FP8;
+    default: return 0;
+  }
+}
+
+size_t codes_bytes(const moe_qweight& q) {
+  const size_t rb = (q.format == MOE_FMT_FP8_B128) ? (size_t)q.cols : (size_t)q.cols / 2;
+  return rb * q.rows;
+}
+size_t scales_bytes(const moe_qweight& q) {
+  switch (q.format) {
+    case MOE_FMT_NVFP4: return (size_t)q.rows * (q.cols / 16);
+    case MOE_FMT_MXFP4: return (size_t)q.rows * (q.cols / 32);
+    default: return (size_t)((q.rows + 127) / 128) * ((q.cols + 127) / 128) * 4;
+  }
+}
+
+// One projection: expected shape [E][rows][cols].
+int32_t check_qweight(const moe_qweight& q, int E, int rows, int cols) {
+  if (fmt_of(q.format) == 0) return MOE_ERR_UNSUPPORTED;
+  if (q.num_experts != E || q.rows != rows || q.cols != cols) return MOE_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (q.format == MOE_FMT_FP8_B128 ? (cols % 16 != 0) : (cols % 32 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (q.codes == nullptr || q.scales == nullptr) return MOE_ERR_INVALID_ARG;
+  if ((q.format == MOE_FMT_NVFP4) != (q.tensor_scale != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(q.codes, 16)) return MOE_ERR_INVALID_ARG;
+  const size_t salign = (q.format == MOE_FMT_FP8_B128) ? 4 : (q.format == MOE_FMT_NVFP4 ? 2 : 1);
+  if (!aligned(q.scales, salign)) return MOE_ERR_INVALID_ARG;
+  if (q.tensor_scale != nullptr && !aligned(q.tensor_scale, 4)) return MOE_ERR_INVALID_ARG;
+  if (E > 1) {
+    if (q.expert_stride_codes < (int64_t)codes_bytes(q) || q.expert_stride_codes % 16 != 0)
+      return MOE_ERR_INVALID_ARG;
+    if (q.expert_stride_scales < (int64_t)scales_bytes(q) ||
+        q.expert_stride_scales % (int64_t)salign != 0)
+      return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+WDesc wdesc(const moe_qweight& q) {
+  WDesc w;
+  w.fmt = fmt_of(q.format);
+  w.codes = q.codes;
+  w.scales = q.scales;
+  w.tscale = q.tensor_scale;
+  w.stride_codes = q.expert_stride_codes;
+  w.stride_scales = q.expert_stride_scales;
+  w.rows = q.rows;
+  w.cols = q.cols;
+  return w;
+}
+
+int32_t check_layer(const moe_layer_desc* L) {
+  if (L == nullptr) return MOE_ERR_INVALID_ARG;
+  if (L->H <= 0 || L->I <= 0 || L->E <= 0 || L->top_k <= 0) return MOE_ERR_INVALID_ARG;
+  if (L->top_k > L->E) return MOE_ERR_INVALID_ARG;
+  if (L->E > kMaxExperts || L->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (L->renormalize != 0 && L->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (L->router_w == nullptr || !aligned(L->router_w, 4)) return MOE_ERR_INVALID_ARG;
+  if (L->router_bias != nullptr && !aligned(L->router_bias, 4)) return MOE_ERR_INVALID_ARG;
+  int32_t st;
+  if ((st = check_qweight(L->gate, L->E, L->I, L->H)) != MOE_OK) return st;
+  if ((st = check_qweight(L->up, L->E, L->I, L->H)) != MOE_OK) return st;
+  if ((st = check_qweight(L->down, L->E, L->H, L->I)) != MOE_OK) return st;
+  if (L->gate.format != L->up.format) return MOE_ERR_UNSUPPORTED;
+  if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (L->has_shared) {
+    if (L->I_shared <= 0) return MOE_ERR_INVALID_ARG;
+    if ((st = check_qweight(L->sh_gate, 1, L->I_shared, L->H)) != MOE_OK) return st;
+    if ((st = check_qweight(L->sh_up, 1, L->I_shared, L->H)) != MOE_OK) return st;
+    if ((st = check_qweight(L->sh_down, 1, L->H, L->I_shared)) != MOE_OK) return st;
+    if (L->sh_gate.format != L->sh_up.format) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+// Workspace sections for (L, T).
+struct WsPlan {
+  RouterPlan rp;
+  int P, NB, max_tiles;
+  size_t part, amax, ids, w, counts, offsets, p2pair, pair2p, hist, act, nact, tiles, ntiles, h,
+      hs, y, ys, total;
+};
+
+constexpr int kTileM = 128;  // rows per grouped-GEMM tile
+
+WsPlan plan(const moe_layer_desc* L, int T) {
+  WsPlan p;
+  const int E = L->E, k = L->top_k;
+  p.rp = router_plan(T, L->H, E);
+  p.P = T * k;
+  p.NB = (p.P + kPermChunk - 1) / kPermChunk;
+  p.max_tiles = p.P / kTileM + (p.P < E ? p.P : E) + 1;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  p.part = take((size_t)p.rp.RS * T * E * 4);
+  p.amax = take((size_t)p.rp.RS * p.rp.CS * T * 4);
+  p.ids = take((size_t)p.P * 4);
+  p.w = take((size_t)p.P * 4);
+  p.counts = take((size_t)E * 4);
+  p.offsets = take((size_t)(E + 1) * 4);
+  p.p2pair = take((size_t)p.P * 4);
+  p.pair2p = take((size_t)p.P * 4);
+  p.hist = take((size_t)p.NB * E * 4);
+  p.act = take((size_t)E * 4);
+  p.nact = take(4);
+  p.tiles = take((size_t)p.max_tiles * 8);
+  p.ntiles = take(4);
+  p.h = take((size_t)p.P * L->I * 2);
+  p.hs = take(L->has_shared ? (size_t)T * L->I_shared * 2 : 0);
+  p.y = take((size_t)p.P * L->H * 4);
+  p.ys = take(L->has_shared ? (size_t)T * L->H * 4 : 0);
+  p.total = o;
+  return p;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off);
+}
+
+thread_local const char* g_last_error = "";
+
+int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_error = hipGetErrorString(e);
+  return MOE_ERR_HIP;
+}
+
+int32_t run_route(const moe_layer_desc* L, const uint16_t* x, float* logits, int T, int* ids,
+                  float* w, void* ws, const WsPlan& p, hipStream_t s) {
+  TopkArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.T = T;
+  a.H = L->H;
+  a.E = L->E;
+  a.k = L->top_k;
+  a.renorm = L->renormalize;
+  a.ids = ids;
+  a.w = w;
+  if (x == nullptr) {
+    a.mode = 0;
+    a.part = logits;
+    a.RS = 1;
+  } else {
+    hipError_t e = launch_router_logits(x, L->router_w, T, L->H, L->E, p.rp, at<float>(ws, p.part),
+                                        at<float>(ws, p.amax), s);
+    if (e != hipSuccess) return hip_status(e);
+    a.mode = 1;
+    a.part = at<float>(ws, p.part);
+    a.RS = p.rp.RS;
+    a.amax = at<float>(ws, p.amax);
+    a.CS = p.rp.CS;
+    a.bias = L->router_bias;
+    a.x = x;
+    a.wr = L->router_w;
+    a.logits_out = logits;
+  }
+  return hip_status(launch_topk(a, s));
+}
+
+int32_t run_experts(int op, const moe_layer_desc* L, int shared, const int* offsets,
+                    const int* perm_to_pair, int T, const uint16_t* in, void* out, void* ws,
+                    const WsPlan& p, bool groups_ready, hipStream_t s) {
+  GroupArgs g;
+  g.offsets = offsets;
+  g.perm_to_pair = perm_to_pair;
+  g.act = at<int>(ws, p.act);
+  g.n_act = at<int>(ws, p.nact);
+  g.topk = L->top_k;
+  g.shared = shared;
+  g.T = T;
+  g.max_groups = p.P < L->E ? p.P : L->E;
+  if (!shared && !groups_ready) {
+    hipError_t e = launch_groups_from_offsets(offsets, L->E, at<int>(ws, p.act), at<int>(ws, p.nact),
+                                              kTileM, at<int>(ws, p.tiles), at<int>(ws, p.ntiles),
+                                              p.max_tiles, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  WDesc w0, w1;
+  if (op == MOE_OP_GATE_UP_SWIGLU) {
+    w0 = wdesc(shared ? L->sh_gate : L->gate);
+    w1 = wdesc(shared ? L->sh_up : L->up);
+  } else {
+    w0 = wdesc(shared ? L->sh_down : L->down);
+    w1 = w0;
+  }
+  return hip_status(launch_expert_gemv(op, w0, w1, g, in, out, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_last_error; }
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_validate_layer(const moe_layer_desc* L) { return check_layer(L); }
+
+size_t moe_workspace_size(const moe_layer_desc* L, int32_t T) {
+  if (check_layer(L) != MOE_OK || T < 0) return 0;
+  if (T == 0) return kAlign;
+  return plan(L, T).total;
+}
+
+int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits, int32_t T,
+                       int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARG;
+  if (x != nullptr && (!aligned(x, 16) || L->H % 8 != 0)) return MOE_ERR_INVALID_ARG;
+  const WsPlan p = plan(L, T);
+  if (x != nullptr && (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)))
+    return MOE_ERR_WORKSPACE;
+  return run_route(L, x, logits, T, topk_ids, topk_w, ws, p, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
+  if (T < 0 || k <= 0 || E <= 0 || E > kMaxExperts) return 0;
+  const PermPlan pp = perm_plan(T, k);
+  return align_up((size_t)pp.NB * E * 4) + align_up((size_t)E * 4) + 2 * kAlign;
+}
+
+int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                    int32_t* offsets, int32_t* perm_to_pair, int32_t* pair_to_perm, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (T < 0 || k <= 0 || E <= 0 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !counts || !offsets || !perm_to_pair || !pair_to_perm) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_permute_workspace_size(T, k, E);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, kAlign)) return MOE_ERR_WORKSPACE;
+  const PermPlan pp = perm_plan(T, k);
+  int* hist = at<int>(ws, 0);
+  int* act = at<int>(ws, align_up((size_t)pp.NB * E * 4));
+  int* nact = at<int>(ws, align_up((size_t)pp.NB * E * 4) + align_up((size_t)E * 4));
+  return hip_status(launch_permute(topk_ids, T, k, E, counts, offsets, perm_to_pair, pair_to_perm,
+                                   hist, act, nact, kTileM, nullptr, nullptr, 0,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
+                        const int32_t* offsets, const int32_t* perm_to_pair, int32_t T,
+                        const uint16_t* in, void* out, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (op != MOE_OP_GATE_UP_SWIGLU && op != MOE_OP_DOWN) return MOE_ERR_INVALID_ARG;
+  if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
+  if (shared && !L->has_shared) return MOE_ERR_INVALID_ARG;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (in == nullptr || out == nullptr || !aligned(in, 16) || !aligned(out, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (!shared && (offsets == nullptr || (op == MOE_OP_GATE_UP_SWIGLU && perm_to_pair == nullptr)))
+    return MOE_ERR_INVALID_ARG;
+  const WsPlan p = plan(L, T);
+  if (!shared && (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)))
+    return MOE_ERR_WORKSPACE;
+  return run_experts(op, L, shared, offsets, perm_to_pair, T, in, out, ws, p, false,
+                     static_cast<hipStream_t>(stream));
+}
+
+int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pair_to_perm,
+                    const float* y_shared, int32_t T, int32_t k, int32_t H, uint16_t* out,
+                    void* stream) {
+  if (T < 0 || k <= 0 || H <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !topk_w || !pair_to_perm || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y_perm, 16) || !aligned(out, 8) || (y_shared && !aligned(y_shared, 16)))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(y_perm, topk_w, pair_to_perm, y_shared, T, k, H, out,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
+                          void* ws, size_t ws_bytes, float* dbg_logits, int32_t* dbg_ids,
+                          float* dbg_w, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || out == nullptr || !aligned(x, 16) || !aligned(out, 16))
+    return MOE_ERR_INVALID_ARG;
+  const WsPlan p = plan(L, T);
+  if (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* ids = dbg_ids ? dbg_ids : at<int>(ws, p.ids);
+  float* w = dbg_w ? dbg_w : at<float>(ws, p.w);
+  if ((st = run_route(L, x, dbg_logits, T, ids, w, ws, p, s)) != MOE_OK) return st;
+  int* offsets = at<int>(ws, p.offsets);
+  int* p2pair = at<int>(ws, p.p2pair);
+  int* pair2p = at<int>(ws, p.pair2p);
+  if ((st = hip_status(launch_permute(ids, T, L->top_k, L->E, at<int>(ws, p.counts), offsets,
+                                      p2pair, pair2p, at<int>(ws, p.hist), at<int>(ws, p.act),
+                                      at<int>(ws, p.nact), kTileM, at<int>(ws, p.tiles),
+                                      at<int>(ws, p.ntiles), p.max_tiles, s))) != MOE_OK)
+    return st;
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  float* y = at<float>(ws, p.y);
+  if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, T, x, h, ws, p, true, s)))
+    return st;
+  if ((st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, T, h, y, ws, p, true, s))) return st;
+  float* ys = nullptr;
+  if (L->has_shared) {
+    uint16_t* hs = at<uint16_t>(ws, p.hs);
+    ys = at<float>(ws, p.ys);
+    if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, T, x, hs, ws, p, true, s)))
+      return st;
+    if ((st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, T, hs, ys, ws, p, true, s)))
+      return st;
+  }
+  return hip_status(launch_combine(y, w, pair2p, ys, T, L->top_k, L->H, out, s));
+}
+
+}  // extern "C"

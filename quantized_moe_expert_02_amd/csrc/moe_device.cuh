@@ -1,0 +1,91 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+enum : int { FMT_NVFP4 = 1, FMT_MXFP4 = 2, FMT_FP8 = 3 };
+
+// One projection of E stacked experts as the kernels see it.
+struct WDesc {
+  int fmt;  // FMT_*
+  const uint8_t* codes;
+  const void* scales;
+  const float* tscale;  // NVFP4 per-expert tensor scale, else nullptr
+  long long stride_codes;   // bytes between experts
+  long long stride_scales;  // bytes between experts
+  int rows, cols;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Pack the upper halves of two floats that are exactly bf16-representable.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Two E4M3 bytes (low 16 bits of w) -> two floats, via the gfx950 converter.
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+}
+
+// Wave-wide helpers --------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ double shfl_xor_d(double v, int m) {
+  return __shfl_xor(v, m, kWave);
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// Launch a kernel and return the status of this launch alone (not the
+// thread's sticky last-error state, which other libraries may have left set).
+template <typename... KArgs, typename... Args, size_t... Is>
+hipError_t launch_impl(void (*k)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                       std::index_sequence<Is...>, Args&&... args) {
+  std::tuple<KArgs...> held(std::forward<Args>(args)...);
+  void* argv[] = {static_cast<void*>(&std::get<Is>(held))..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, shmem, s);
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*k)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                  Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  return launch_impl(k, grid, block, shmem, s, std::index_sequence_for<KArgs...>{},
+                     std::forward<Args>(args)...);
+}
+
+}  // namespace moe

@@ -1,0 +1,83 @@
+// Host-side launchers of the MoE kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_device.cuh"
+
+namespace moe {
+
+// ---- routing --------------------------------------------------------------
+// Rows of the router per partial-sum slice and experts per block.
+constexpr int kRouterCols = 32;
+constexpr int kRouterTokens = 8;
+constexpr int kMaxExperts = 1024;  // top-k keeps up to 16 logits per lane
+constexpr int kMaxTopK = 32;
+
+struct RouterPlan {
+  int RH;  // router rows per slice
+  int RS;  // number of slices
+  int CS;  // number of column blocks
+};
+RouterPlan router_plan(int T, int H, int E);
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E,
+                                const RouterPlan& rp, float* part, float* amax, hipStream_t s);
+
+struct TopkArgs {
+  const float* part;  // mode 1: partial logits [RS][T][E]; mode 0: given logits [T][E]
+  int RS;
+  const float* amax;  // mode 1: [RS][CS][T]
+  int CS;
+  const float* bias;  // [E] or nullptr (mode 1)
+  const uint16_t* x;  // mode 1: activations for the certified recompute
+  const float* wr;
+  int mode;
+  int T, H, E, k, renorm;
+  float* logits_out;  // [T][E] or nullptr
+  int* ids;           // [T][k]
+  float* w;           // [T][k]
+  int* recomputed;    // [T] or nullptr
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// ---- grouping -------------------------------------------------------------
+constexpr int kPermChunk = 1024;
+struct PermPlan {
+  int P, NB;
+};
+inline PermPlan perm_plan(int T, int k) {
+  PermPlan p;
+  p.P = T * k;
+  p.NB = (p.P + kPermChunk - 1) / kPermChunk;
+  return p;
+}
+// ws: hist [NB][E] int32 (base offsets written back in place)
+hipError_t launch_permute(const int* ids, int T, int k, int E, int* counts, int* offsets,
+                          int* perm_to_pair, int* pair_to_perm, int* hist, int* act,
+                          int* n_act, int tile_m, int* tiles, int* n_tiles, int max_tiles,
+                          hipStream_t s);
+// Active-expert list (and tile list) from offsets only.
+hipError_t launch_groups_from_offsets(const int* offsets, int E, int* act, int* n_act, int tile_m,
+                                      int* tiles, int* n_tiles, int max_tiles, hipStream_t s);
+
+// ---- experts ----------------------------------------------------------------
+struct GroupArgs {
+  const int* offsets;       // [E+1] (routed)
+  const int* perm_to_pair;  // routed GATE_UP input-row map
+  const int* act;           // active expert ids
+  const int* n_act;
+  int topk;
+  int shared;  // 1: single expert over rows 0..T-1
+  int T;
+  int max_groups;  // grid bound on active experts
+};
+hipError_t launch_expert_gemv(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
+                              const uint16_t* in, void* out, hipStream_t s);
+
+// ---- combine ----------------------------------------------------------------
+hipError_t launch_combine(const float* y, const float* w, const int* pair_to_perm, const float* ys,
+                          int T, int k, int H, uint16_t* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,162 @@
+// Token-to-expert grouping: a stable counting sort of the (token, slot) pairs.
+//
+// The grouped expert GEMM runs "over a compact list of the routed segments'
+// tiles instead of a grid over the longest segment" (gitee "dgpp" README,
+// "Execution and performance", engine.expert_tile_list).  The segments are
+// built here deterministically: counts come from per-chunk histograms (LDS
+// integer atomics, order-free), offsets from a scan, and each pair's rank in
+// its segment from a scan over chunks plus an in-order rank within the chunk,
+// so the permutation is the same on every run.
+#include "moe_launch.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, int P, int E,
+                                                   int* __restrict__ hist) {
+  __shared__ int cnt[kMaxExperts];
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int p0 = b * kPermChunk, p1 = min(P, p0 + kPermChunk);
+  for (int p = p0 + threadIdx.x; p < p1; p += 256) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);  // out-of-range ids are dropped
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[(size_t)b * E + e] = cnt[e];
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads).
+__device__ int block_exclusive_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      const int s = tmp[w];
+      tmp[w] = run;
+      run += s;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  const int r = tmp[wave] + x - v;
+  total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
+// One block of 1024 threads, thread e owns expert e (E <= 1024).
+__global__ __launch_bounds__(1024) void scan_kernel(int NB, int E, int* __restrict__ hist,
+                                                    int* __restrict__ counts,
+                                                    int* __restrict__ offsets,
+                                                    int* __restrict__ act, int* __restrict__ n_act,
+                                                    int tile_m, int2* __restrict__ tiles,
+                                                    int* __restrict__ n_tiles, int max_tiles,
+                                                    int from_offsets) {
+  __shared__ int tmp[17];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (from_offsets) {
+    if (e < E) c = offsets[e + 1] - offsets[e];
+  } else if (e < E) {
+    for (int b = 0; b < NB; ++b) {
+      const int h = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = c;  // rank base of chunk b within expert e
+      c += h;
+    }
+    counts[e] = c;
+  }
+  int total;
+  const int off = block_exclusive_scan(e < E ? c : 0, tmp, total);
+  if (!from_offsets) {
+    if (e < E) {
+      offsets[e] = off;
+      for (int b = 0; b < NB; ++b) hist[(size_t)b * E + e] += off;
+    }
+    if (e == 0) offsets[E] = total;
+  }
+  // active experts in increasing id order
+  int nact;
+  const int ai = block_exclusive_scan((e < E && c > 0) ? 1 : 0, tmp, nact);
+  if (e < E && c > 0) act[ai] = e;
+  if (e == 0) *n_act = nact;
+  if (tiles != nullptr) {
+    const int nt_e = (e < E) ? (c + tile_m - 1) / tile_m : 0;
+    int ntot;
+    const int t0 = block_exclusive_scan(nt_e, tmp, ntot);
+    const int base = (e < E) ? (from_offsets ? offsets[e] : off) : 0;
+    for (int i = 0; i < nt_e; ++i)
+      if (t0 + i < max_tiles) tiles[t0 + i] = make_int2(e, base + i * tile_m);
+    if (e == 0) *n_tiles = ntot < max_tiles ? ntot : max_tiles;
+  }
+}
+
+// One wave per chunk; the chunk's pairs are ranked 64 at a time in order.
+__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids, int P, int E,
+                                                     const int* __restrict__ base,
+                                                     int* __restrict__ perm_to_pair,
+                                                     int* __restrict__ pair_to_perm) {
+  __shared__ int cnt[kMaxExperts];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = base[(size_t)b * E + e];
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int p0 = b * kPermChunk, p1 = min(P, p0 + kPermChunk);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s = p0; s < p1; s += 64) {
+    const int p = s + lane;
+    const int e0 = (p < p1) ? ids[p] : -1;
+    const bool valid = (p < p1) && (unsigned)e0 < (unsigned)E;
+    const int e = valid ? e0 : -1;
+    // lanes holding the same expert id
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t m = __ballot(valid && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(same & lt);
+    int pos = 0;
+    if (valid) pos = cnt[e] + rank;
+    __syncthreads();
+    if (valid) {
+      perm_to_pair[pos] = p;
+      pair_to_perm[p] = pos;
+      // the last lane of each group advances the counter
+      if ((same >> lane) == 1ull) cnt[e] = pos + 1;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const int* ids, int T, int k, int E, int* counts, int* offsets,
+                          int* perm_to_pair, int* pair_to_perm, int* hist, int* act, int* n_act,
+                          int tile_m, int* tiles, int* n_tiles, int max_tiles, hipStream_t s) {
+  const PermPlan pp = perm_plan(T, k);
+  hipError_t e = launch(hist_kernel, dim3(pp.NB), dim3(256), 0, s, ids, pp.P, E, hist);
+  if (e != hipSuccess) return e;
+  e = launch(scan_kernel, dim3(1), dim3(1024), 0, s, pp.NB, E, hist, counts, offsets, act, n_act,
+             tile_m, reinterpret_cast<int2*>(tiles), n_tiles, max_tiles, 0);
+  if (e != hipSuccess) return e;
+  return launch(scatter_kernel, dim3(pp.NB), dim3(64), 0, s, ids, pp.P, E, hist, perm_to_pair,
+                pair_to_perm);
+}
+
+hipError_t launch_groups_from_offsets(const int* offsets, int E, int* act, int* n_act, int tile_m,
+                                      int* tiles, int* n_tiles, int max_tiles, hipStream_t s) {
+  return launch(scan_kernel, dim3(1), dim3(1024), 0, s, 0, E, nullptr, nullptr,
+                const_cast<int*>(offsets), act, n_act, tile_m, reinterpret_cast<int2*>(tiles),
+                n_tiles, max_tiles, 1);
+}
+
+}  // namespace moe

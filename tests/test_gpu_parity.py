@@ -1,0 +1,171 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import formats as F
+from oracle import layer as O
+
+from gpu_util import assert_close, check_layer_against_oracle, device_layer, layer_for, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU-only hosts too
+    pytest.skip("no GPU", allow_module_level=True)
+
+import quantized_moe_expert_02_amd as moe  # noqa: E402
+from quantized_moe_expert_02_amd.device import bf16_bits, bf16_tensor  # noqa: E402
+
+W = synth.WORKLOADS
+
+# Small layers that still span several tiles, with ragged K chunks and row tiles.
+SMALL = {
+    "nvfp4_ragged": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_ragged", T=5, H=352, E=24, I=160,
+                                 top_k=3, I_shared=96, shared_fmt=synth.FMT_FP8),
+    "mxfp4_ragged": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp4_ragged", T=7, H=416, E=20, I=224,
+                                 top_k=4, fmt=synth.FMT_MXFP4, I_shared=64,
+                                 shared_fmt=synth.FMT_NVFP4, zipf_s=1.1),
+    "fp8_ragged": synth.scaled(W["tiny_nvfp4_t4"], name="fp8_ragged", T=8, H=336, E=12, I=144,
+                               top_k=2, fmt=synth.FMT_FP8, I_shared=272, shared_fmt=synth.FMT_FP8),
+    "nvfp4_t3_k1": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t3_k1", T=3, H=256, E=4, I=128,
+                                top_k=1),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny_nvfp4_t4"] + list(SMALL))
+def test_layer_small(name):
+    w = W.get(name) or SMALL[name]
+    say(f"[gpu] layer {name}: T={w.T} H={w.H} E={w.E} I={w.I} k={w.top_k} fmt={w.fmt}")
+    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), what=name)
+    say(f"[gpu] layer {name}: rel={r['rel']:.2e} worst={r['worst']:.2e}")
+
+
+@pytest.mark.parametrize("name", ["decode_t1_nvfp4", "decode_t8_nvfp4_zipf", "decode_t8_mxfp4_zipf"])
+def test_layer_decode_full(name):
+    w = W[name]
+    say(f"[gpu] layer {name} (full size)")
+    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), what=name)
+    say(f"[gpu] layer {name}: rel={r['rel']:.2e} worst={r['worst']:.2e} "
+        f"unique experts={len(np.unique(r['ids']))}")
+
+
+def test_layer_decode_fp8_wide_sampled():
+    w = W["decode_t8_fp8_wide"]
+    say("[gpu] layer decode_t8_fp8_wide (full size, outputs of tokens 0 and 5)")
+    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), tokens=[0, 5],
+                                   what="decode_t8_fp8_wide")
+    say(f"[gpu] fp8 wide: rel={r['rel']:.2e} worst={r['worst']:.2e}")
+
+
+def test_layer_is_deterministic():
+    w = SMALL["nvfp4_ragged"]
+    dl = device_layer(layer_for(w))
+    from gpu_util import run_layer
+    x = synth.make_x(w)
+    a = run_layer(dl, x)
+    b = run_layer(dl, x)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v, equal_nan=True)
+
+
+def test_route_topk_given_logits_exact():
+    rng = np.random.default_rng(11)
+    T, E, k = 37, 64, 6
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, [5, 9, 40]] = 9.0
+    logits[1, :] = 0.5
+    logits[2, [1, 2]] = np.nan
+    logits[3, 17] = np.inf
+    w_ = synth.scaled(W["tiny_nvfp4_t4"], name="route", E=E, top_k=k)
+    dl = device_layer(layer_for(w_))
+    lg = torch.from_numpy(logits).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route_topk(dl.desc, None, lg, T, ids, wt, dl.workspace(T))
+    torch.cuda.synchronize()
+    ref_ids, ref_w = O.route_from_logits(logits, k, True)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ok = np.all(np.isfinite(ref_w), axis=1)
+    assert_close(wt.cpu().numpy()[ok], ref_w[ok], "given-logit weights")
+
+
+@pytest.mark.parametrize("T,k,E,skew", [(1, 10, 512, 0), (8, 10, 512, 1), (300, 7, 96, 1),
+                                        (8192, 10, 512, 1), (1500, 1, 3, 0)])
+def test_permute_bit_exact(T, k, E, skew):
+    say(f"[gpu] permute T={T} k={k} E={E} skew={skew}")
+    rng = np.random.default_rng(T * 31 + E)
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)])
+    else:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    ids = ids.astype(np.int32)
+    ref = O.permute(ids, E)
+    d = torch.from_numpy(ids).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    p2 = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    q2 = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.moe_permute_workspace_size(T, k, E), dtype=torch.uint8, device="cuda")
+    moe.moe_permute(d, T, k, E, counts, offsets, p2, q2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), ref.counts)
+    assert np.array_equal(offsets.cpu().numpy(), ref.offsets)
+    assert np.array_equal(p2.cpu().numpy(), ref.perm_to_pair)
+    assert np.array_equal(q2.cpu().numpy(), ref.pair_to_perm)
+
+
+@pytest.mark.parametrize("name", ["nvfp4_ragged", "mxfp4_ragged", "fp8_ragged"])
+def test_expert_gemm_and_combine_units(name):
+    """Each unit entry point alone, fed the oracle's own routing."""
+    w = SMALL[name]
+    L = layer_for(w)
+    x_bits = synth.make_x(w)
+    ref = O.layer_forward(L, x_bits)
+    G = ref.grouping
+    dl = device_layer(L)
+    T, k, H, I = w.T, w.top_k, w.H, w.I
+    P = T * k
+    x = bf16_tensor(x_bits)
+    offs = torch.from_numpy(G.offsets).cuda()
+    p2 = torch.from_numpy(G.perm_to_pair).cuda()
+    q2 = torch.from_numpy(G.pair_to_perm).cuda()
+    ws = dl.workspace(T)
+    h = torch.empty((P, I), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, dl.desc, 0, offs, p2, T, x, h, ws)
+    torch.cuda.synchronize()
+    pairs = G.perm_to_pair
+    ref_h = ref.h.reshape(P, I)[pairs]           # oracle h in permuted order
+    got_h = O.bf16_value(bf16_bits(h))
+    assert_close(got_h, ref_h, name + " h")
+    # down on the oracle's h
+    hin = bf16_tensor(O.bf16_bits(ref_h))
+    y = torch.empty((P, H), dtype=torch.float32, device="cuda")
+    moe.moe_expert_gemm(moe.MOE_OP_DOWN, dl.desc, 0, offs, p2, T, hin, y, ws)
+    torch.cuda.synchronize()
+    yp = np.zeros((P, H))
+    for e in np.unique(ref.routing.ids):
+        rows = np.arange(G.offsets[e], G.offsets[e + 1])
+        yp[rows] = O.ffn_down(ref_h[rows], F.dequant(L.down, int(e)))
+    assert_close(y.cpu().numpy(), yp, name + " y")
+    # shared expert
+    ys = None
+    if L.has_shared:
+        hs = torch.empty((T, w.I_shared), dtype=torch.bfloat16, device="cuda")
+        moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, dl.desc, 1, None, None, T, x, hs, ws)
+        ys = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        moe.moe_expert_gemm(moe.MOE_OP_DOWN, dl.desc, 1, None, None, T,
+                            bf16_tensor(O.bf16_bits(ref.h_shared)), ys, ws)
+        torch.cuda.synchronize()
+        assert_close(O.bf16_value(bf16_bits(hs)), ref.h_shared, name + " shared h")
+        assert_close(ys.cpu().numpy(), ref.y_shared, name + " shared y")
+    # combine on the oracle's partials
+    yperm = torch.from_numpy(ref.y.reshape(P, H)[pairs].astype(np.float32)).cuda()
+    wt = torch.from_numpy(ref.routing.weights.astype(np.float32)).cuda()
+    ysh = torch.from_numpy(ref.y_shared.astype(np.float32)).cuda() if L.has_shared else None
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(yperm, wt, q2, ysh, T, k, H, out)
+    torch.cuda.synchronize()
+    assert_close(O.bf16_value(bf16_bits(out)), ref.out, name + " combine")
