@@ -109,8 +109,9 @@ int32_t moe_validate_layer(const moe_layer_desc* L);
 
 /* Workspace bytes every entry point below needs for this layer and T tokens.
  * A workspace of at least this size (256-byte aligned device memory) serves
- * any call with the same (L, T); it needs no initialisation.  Returns 0 when
- * the descriptor is invalid. */
+ * any call with the same (L, T) or smaller T; it needs no initialisation.
+ * Calls that share a workspace must not overlap in time.  Returns 0 when the
+ * descriptor is invalid. */
 size_t moe_workspace_size(const moe_layer_desc* L, int32_t T);
 
 /* Router softmax + top-k (the router function, top-k and tie rule are not on
@@ -131,21 +132,26 @@ int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits
 
 /* Grouping of the T*k (token, slot) pairs by expert: a stable counting sort
  * (pairs in t-major, slot order within each expert).
- *   topk_ids int32 [T][k] with values in [0, E) (other values: undefined).
+ *   topk_ids int32 [T][k] with values in [0, E) (out-of-range ids are dropped).
  *   counts [E]; offsets [E+1] (exclusive scan of counts);
  *   perm_to_pair [T*k]: permuted row -> pair t*k+j; pair_to_perm [T*k]: inverse.
+ *   active_experts int32 [E+1] or NULL: element 0 = number of experts with at
+ *            least one row, then their ids in increasing order.
  * Workspace: moe_permute_workspace_size(T, k, E) bytes. */
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
 int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
-                    int32_t* offsets, int32_t* perm_to_pair, int32_t* pair_to_perm, void* ws,
-                    size_t ws_bytes, void* stream);
+                    int32_t* offsets, int32_t* perm_to_pair, int32_t* pair_to_perm,
+                    int32_t* active_experts, void* ws, size_t ws_bytes, void* stream);
 
 /* One expert projection pass over grouped rows.
  *   shared = 0: routed experts; rows are the T*k permuted pairs grouped by
  *     `offsets` [E+1]; for op GATE_UP the input row of permuted row p is
  *     token perm_to_pair[p]/k of `in` (x bf16 [T][H]); for op DOWN the input
  *     row is p of `in` (h bf16 [T*k][I]).  Output row p in permuted order.
- *   shared = 1: the shared expert over T rows of `in`; offsets/perm_to_pair unused.
+ *   active_experts: routed only, the [E+1] list moe_permute writes (count,
+ *     then ids); NULL derives it from `offsets` with one extra launch.
+ *   shared = 1: the shared expert over T rows of `in`; offsets, perm_to_pair
+ *     and active_experts unused.
  *   out: GATE_UP -> bf16 [rows][I or I_shared]; DOWN -> fp32 [rows][H].
  * Accumulation is fp32; products of the decoded weight and the bf16 input are
  * exact.  The intermediate h is BF16 (activations stay BF16, forum opening
@@ -153,8 +159,9 @@ int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, in
  * "dgpp" README, "Highlights"): groups of up to 16 rows stream weights once
  * per group, larger groups run as tiled grouped GEMM. */
 int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
-                        const int32_t* offsets, const int32_t* perm_to_pair, int32_t T,
-                        const uint16_t* in, void* out, void* ws, size_t ws_bytes, void* stream);
+                        const int32_t* offsets, const int32_t* perm_to_pair,
+                        const int32_t* active_experts, int32_t T, const uint16_t* in, void* out,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Weighted combine (partials kept in fp32, summed in slot order; bf16
  * partials are a lossy lever on the pages, gitee "dgpp" README, "Execution

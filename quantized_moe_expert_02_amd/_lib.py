@@ -74,8 +74,8 @@ def _load():
         "moe_workspace_size": (SZ, [LP, I32]),
         "moe_route_topk": (I32, [LP, P, P, I32, P, P, P, SZ, P]),
         "moe_permute_workspace_size": (SZ, [I32, I32, I32]),
-        "moe_permute": (I32, [P, I32, I32, I32, P, P, P, P, P, SZ, P]),
-        "moe_expert_gemm": (I32, [I32, LP, I32, P, P, I32, P, P, P, SZ, P]),
+        "moe_permute": (I32, [P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
+        "moe_expert_gemm": (I32, [I32, LP, I32, P, P, P, I32, P, P, P, SZ, P]),
         "moe_combine": (I32, [P, P, P, P, I32, I32, I32, P, P]),
         "moe_layer_forward": (I32, [LP, P, I32, P, P, SZ, P, P, P, P]),
     }
@@ -140,19 +140,19 @@ def moe_route_topk(L, x, logits, T, topk_ids, topk_w, ws, ws_bytes=None, stream=
     return _check(st, "moe_route_topk") if check else st
 
 
-def moe_permute(topk_ids, T, k, E, counts, offsets, perm_to_pair, pair_to_perm, ws, ws_bytes=None,
-                stream=None, check=True):
+def moe_permute(topk_ids, T, k, E, counts, offsets, perm_to_pair, pair_to_perm, active_experts, ws,
+                ws_bytes=None, stream=None, check=True):
     wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
     st = LIB.moe_permute(_p(topk_ids), T, k, E, _p(counts), _p(offsets), _p(perm_to_pair),
-                         _p(pair_to_perm), _p(ws), wsb, _stream(stream))
+                         _p(pair_to_perm), _p(active_experts), _p(ws), wsb, _stream(stream))
     return _check(st, "moe_permute") if check else st
 
 
-def moe_expert_gemm(op, L, shared, offsets, perm_to_pair, T, inp, out, ws, ws_bytes=None,
-                    stream=None, check=True):
+def moe_expert_gemm(op, L, shared, offsets, perm_to_pair, active_experts, T, inp, out, ws,
+                    ws_bytes=None, stream=None, check=True):
     wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    st = LIB.moe_expert_gemm(op, ctypes.byref(L), shared, _p(offsets), _p(perm_to_pair), T, _p(inp),
-                             _p(out), _p(ws), wsb, _stream(stream))
+    st = LIB.moe_expert_gemm(op, ctypes.byref(L), shared, _p(offsets), _p(perm_to_pair),
+                             _p(active_experts), T, _p(inp), _p(out), _p(ws), wsb, _stream(stream))
     return _check(st, "moe_expert_gemm") if check else st
 
 

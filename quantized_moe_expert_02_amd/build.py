@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "expert_gemv.hip",
+SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "expert_gemv.hip", "decode.hip",
            "combine.hip"]
 ARCH = "gfx950"
 

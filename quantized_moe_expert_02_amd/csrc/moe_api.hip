@@ -104,10 +104,15 @@ int32_t check_layer(const moe_layer_desc* L) {
 // Workspace sections for (L, T).
 struct WsPlan {
   RouterPlan rp;
+  DecodePlan dp;
   int P, NB, max_tiles;
   size_t part, amax, ids, w, counts, offsets, p2pair, pair2p, hist, act, nact, tiles, ntiles, h,
       hs, y, ys, total;
+  // fused decode (T <= kDecodeRows): router slice sums
+  size_t dpart, dapart;
 };
+
+constexpr int kDecodeRows = 8;
 
 constexpr int kTileM = 128;  // rows per grouped-GEMM tile
 
@@ -124,6 +129,7 @@ WsPlan plan(const moe_layer_desc* L, int T) {
     o += align_up(bytes);
     return at;
   };
+  p.dp = decode_plan(T, L->H, E);
   p.part = take((size_t)p.rp.RS * T * E * 4);
   p.amax = take((size_t)p.rp.RS * p.rp.CS * T * 4);
   p.ids = take((size_t)p.P * 4);
@@ -133,14 +139,19 @@ WsPlan plan(const moe_layer_desc* L, int T) {
   p.p2pair = take((size_t)p.P * 4);
   p.pair2p = take((size_t)p.P * 4);
   p.hist = take((size_t)p.NB * E * 4);
-  p.act = take((size_t)E * 4);
-  p.nact = take(4);
+  p.nact = take((size_t)(E + 1) * 4);  // [0] = count, then ids
+  p.act = p.nact + 4;
   p.tiles = take((size_t)p.max_tiles * 8);
   p.ntiles = take(4);
   p.h = take((size_t)p.P * L->I * 2);
   p.hs = take(L->has_shared ? (size_t)T * L->I_shared * 2 : 0);
   p.y = take((size_t)p.P * L->H * 4);
   p.ys = take(L->has_shared ? (size_t)T * L->H * 4 : 0);
+  p.dpart = p.dapart = 0;
+  if (T <= kDecodeRows) {
+    p.dpart = take((size_t)p.dp.RS * T * E * 4);
+    p.dapart = take((size_t)p.dp.RS * T * E * 4);
+  }
   p.total = o;
   return p;
 }
@@ -191,21 +202,24 @@ int32_t run_route(const moe_layer_desc* L, const uint16_t* x, float* logits, int
 }
 
 int32_t run_experts(int op, const moe_layer_desc* L, int shared, const int* offsets,
-                    const int* perm_to_pair, int T, const uint16_t* in, void* out, void* ws,
-                    const WsPlan& p, bool groups_ready, hipStream_t s) {
+                    const int* perm_to_pair, const int* active, int T, const uint16_t* in,
+                    void* out, void* ws, const WsPlan& p, hipStream_t s) {
   GroupArgs g;
   g.offsets = offsets;
   g.perm_to_pair = perm_to_pair;
-  g.act = at<int>(ws, p.act);
-  g.n_act = at<int>(ws, p.nact);
+  const bool groups_ready = shared || active != nullptr;
+  if (active == nullptr && !shared) active = at<int>(ws, p.nact);
+  g.act = active ? active + 1 : nullptr;
+  g.n_act = active;
   g.topk = L->top_k;
   g.shared = shared;
   g.T = T;
+  g.E = L->E;
   g.max_groups = p.P < L->E ? p.P : L->E;
   if (!shared && !groups_ready) {
-    hipError_t e = launch_groups_from_offsets(offsets, L->E, at<int>(ws, p.act), at<int>(ws, p.nact),
-                                              kTileM, at<int>(ws, p.tiles), at<int>(ws, p.ntiles),
-                                              p.max_tiles, s);
+    hipError_t e = launch_groups_from_offsets(offsets, L->E, at<int>(ws, p.act),
+                                              at<int>(ws, p.nact), kTileM, at<int>(ws, p.tiles),
+                                              at<int>(ws, p.ntiles), p.max_tiles, s);
     if (e != hipSuccess) return hip_status(e);
   }
   WDesc w0, w1;
@@ -263,12 +277,12 @@ int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
   if (T < 0 || k <= 0 || E <= 0 || E > kMaxExperts) return 0;
   const PermPlan pp = perm_plan(T, k);
-  return align_up((size_t)pp.NB * E * 4) + align_up((size_t)E * 4) + 2 * kAlign;
+  return align_up((size_t)pp.NB * E * 4) + align_up((size_t)(E + 1) * 4);
 }
 
 int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
-                    int32_t* offsets, int32_t* perm_to_pair, int32_t* pair_to_perm, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    int32_t* offsets, int32_t* perm_to_pair, int32_t* pair_to_perm,
+                    int32_t* active_experts, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || k <= 0 || E <= 0 || k > E) return MOE_ERR_INVALID_ARG;
   if (E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
@@ -277,16 +291,16 @@ int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, in
   if (ws == nullptr || ws_bytes < need || !aligned(ws, kAlign)) return MOE_ERR_WORKSPACE;
   const PermPlan pp = perm_plan(T, k);
   int* hist = at<int>(ws, 0);
-  int* act = at<int>(ws, align_up((size_t)pp.NB * E * 4));
-  int* nact = at<int>(ws, align_up((size_t)pp.NB * E * 4) + align_up((size_t)E * 4));
+  int* active = active_experts ? active_experts : at<int>(ws, align_up((size_t)pp.NB * E * 4));
   return hip_status(launch_permute(topk_ids, T, k, E, counts, offsets, perm_to_pair, pair_to_perm,
-                                   hist, act, nact, kTileM, nullptr, nullptr, 0,
+                                   hist, active + 1, active, kTileM, nullptr, nullptr, 0,
                                    static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
-                        const int32_t* offsets, const int32_t* perm_to_pair, int32_t T,
-                        const uint16_t* in, void* out, void* ws, size_t ws_bytes, void* stream) {
+                        const int32_t* offsets, const int32_t* perm_to_pair,
+                        const int32_t* active_experts, int32_t T, const uint16_t* in, void* out,
+                        void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_layer(L);
   if (st != MOE_OK) return st;
   if (op != MOE_OP_GATE_UP_SWIGLU && op != MOE_OP_DOWN) return MOE_ERR_INVALID_ARG;
@@ -301,8 +315,8 @@ int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
   const WsPlan p = plan(L, T);
   if (!shared && (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)))
     return MOE_ERR_WORKSPACE;
-  return run_experts(op, L, shared, offsets, perm_to_pair, T, in, out, ws, p, false,
-                     static_cast<hipStream_t>(stream));
+  return run_experts(op, L, shared, offsets, perm_to_pair, shared ? nullptr : active_experts, T,
+                     in, out, ws, p, static_cast<hipStream_t>(stream));
 }
 
 int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pair_to_perm,
@@ -332,6 +346,43 @@ int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T,
   hipStream_t s = static_cast<hipStream_t>(stream);
   int* ids = dbg_ids ? dbg_ids : at<int>(ws, p.ids);
   float* w = dbg_w ? dbg_w : at<float>(ws, p.w);
+  if (T <= kDecodeRows) {
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.T = T;
+    a.H = L->H;
+    a.I = L->I;
+    a.E = L->E;
+    a.k = L->top_k;
+    a.renorm = L->renormalize;
+    a.I_shared = L->has_shared ? L->I_shared : 0;
+    a.has_shared = L->has_shared;
+    a.max_groups = p.P < L->E ? p.P : L->E;
+    a.wr = L->router_w;
+    a.bias = L->router_bias;
+    a.gate = wdesc(L->gate);
+    a.up = wdesc(L->up);
+    a.down = wdesc(L->down);
+    if (L->has_shared) {
+      a.sg = wdesc(L->sh_gate);
+      a.su = wdesc(L->sh_up);
+      a.sd = wdesc(L->sh_down);
+    }
+    a.RS = p.dp.RS;
+    a.CS = p.dp.CS;
+    a.part = at<float>(ws, p.dpart);
+    a.apart = at<float>(ws, p.dapart);
+    a.logits_out = dbg_logits;
+    a.ids = ids;
+    a.w = w;
+    a.h = at<uint16_t>(ws, p.h);
+    a.hs = L->has_shared ? at<uint16_t>(ws, p.hs) : nullptr;
+    a.y = at<float>(ws, p.y);
+    a.ys = L->has_shared ? at<float>(ws, p.ys) : nullptr;
+    a.out = out;
+    return hip_status(launch_decode(a, s));
+  }
   if ((st = run_route(L, x, dbg_logits, T, ids, w, ws, p, s)) != MOE_OK) return st;
   int* offsets = at<int>(ws, p.offsets);
   int* p2pair = at<int>(ws, p.p2pair);
@@ -343,16 +394,18 @@ int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T,
     return st;
   uint16_t* h = at<uint16_t>(ws, p.h);
   float* y = at<float>(ws, p.y);
-  if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, T, x, h, ws, p, true, s)))
+  const int* active = at<int>(ws, p.nact);
+  if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, x, h, ws, p, s)))
     return st;
-  if ((st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, T, h, y, ws, p, true, s))) return st;
+  if ((st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, h, y, ws, p, s))) return st;
   float* ys = nullptr;
   if (L->has_shared) {
     uint16_t* hs = at<uint16_t>(ws, p.hs);
     ys = at<float>(ws, p.ys);
-    if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, T, x, hs, ws, p, true, s)))
+    if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T, x, hs, ws, p,
+                          s)))
       return st;
-    if ((st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, T, hs, ys, ws, p, true, s)))
+    if ((st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hs, ys, ws, p, s)))
       return st;
   }
   return hip_status(launch_combine(y, w, pair2p, ys, T, L->top_k, L->H, out, s));

@@ -71,10 +71,38 @@ struct GroupArgs {
   int topk;
   int shared;  // 1: single expert over rows 0..T-1
   int T;
+  int E;
   int max_groups;  // grid bound on active experts
 };
 hipError_t launch_expert_gemv(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
                               const uint16_t* in, void* out, hipStream_t s);
+
+// ---- fused decode lowering (T <= 8) -----------------------------------------
+struct DecodePlan {
+  int RS, CS, down_tiles;
+};
+DecodePlan decode_plan(int T, int H, int E);
+
+struct DecodeArgs {
+  const uint16_t* x;
+  int T, H, I, E, k, renorm, I_shared, has_shared, max_groups;
+  const float* wr;
+  const float* bias;
+  WDesc gate, up, down, sg, su, sd;
+  int RS, CS;
+  // workspace
+  float* part;        // [RS][T][E] fp32 slice sums of x.Wr
+  float* apart;       // [RS][T][E] fp32 slice sums of |x||Wr|
+  float* logits_out;  // [T][E] debug copy or nullptr
+  int* ids;           // [T][k]
+  float* w;           // [T][k]
+  uint16_t* h;        // [T*k][I], row = pair t*k+j
+  uint16_t* hs;       // [T][I_shared]
+  float* y;           // [T*k][H], row = pair t*k+j
+  float* ys;          // [T][H]
+  uint16_t* out;      // [T][H]
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------------
 hipError_t launch_combine(const float* y, const float* w, const int* pair_to_perm, const float* ys,

@@ -13,18 +13,17 @@
 // accepts the fast order when every adjacent gap among the top k+1 exceeds
 // twice that bound; otherwise it recomputes the contested logits with a
 // compensated (double-float64) sum and decides on those.
-#include <climits>
-
 #include "moe_launch.h"
+#include "topk_core.cuh"
 
 namespace moe {
 
 RouterPlan router_plan(int T, int H, int E) {
   RouterPlan p;
-  // Decode sizes: many slices so that a few hundred workgroups stream the
-  // router weights once.  Prefill: one slice (the partial is the full sum).
-  p.RH = (T <= kRouterTokens) ? 128 : H;
-  if (p.RH > H) p.RH = H;
+  // One slice: each block sums the whole contraction for its 32 experts and
+  // 8 tokens, so the partial is the full sum.
+  (void)T;
+  p.RH = H;
   p.RS = (H + p.RH - 1) / p.RH;
   p.CS = (E + kRouterCols - 1) / kRouterCols;
   return p;
@@ -102,194 +101,52 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
-// Selection key: class 2 = a number (incl. +-inf), 1 = NaN, 0 = not eligible.
-__device__ __forceinline__ bool better(int ca, double va, int ia, int cb, double vb, int ib) {
-  if (ca != cb) return ca > cb;
-  if (ca == 2 && va != vb) return va > vb;
-  return ia < ib;
-}
-
-__device__ __forceinline__ void two_sum(double a, double b, double& s, double& err) {
-  s = a + b;
-  const double bp = s - a;
-  const double ap = s - bp;
-  err = (a - ap) + (b - bp);
-}
-
-// Compensated float64 logit of expert e for one token (whole wave).
-__device__ double dd_logit(const uint16_t* __restrict__ xrow, const float* __restrict__ wr, int H,
-                           int E, int e, const float* bias) {
-  const int lane = __lane_id();
-  double s = 0.0, c = 0.0;
-  for (int h = lane; h < H; h += kWave) {
-    const double p = static_cast<double>(bf16_to_f32(xrow[h])) *
-                     static_cast<double>(wr[(size_t)h * E + e]);
-    double err;
-    two_sum(s, p, s, err);
-    c += err;
-  }
-  // Pairwise combine; both lanes of a pair compute the same values, so every
-  // lane ends with the same result.
-  for (int m = 1; m < kWave; m <<= 1) {
-    const double os = __shfl_xor(s, m, kWave);
-    const double oc = __shfl_xor(c, m, kWave);
-    double err;
-    two_sum(s, os, s, err);
-    c = (c + oc) + err;
-  }
-  if (bias != nullptr) {
-    double err;
-    two_sum(s, static_cast<double>(bias[e]), s, err);
-    c += err;
-  }
-  return s + c;
-}
-
-constexpr int kEPL = kMaxExperts / kWave;  // logits per lane
-
-__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  (void)wave;
-  if (t >= a.T) return;  // no block-level barrier below: waves are independent
-  const int E = a.E, k = a.k;
-
-  double v[kEPL];
-  uint32_t nanmask = 0;
-#pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
-    const int e = lane + kWave * i;
-    double val = 0.0;
-    if (e < E) {
-      if (a.mode == 0) {
-        val = static_cast<double>(a.part[(size_t)t * E + e]);
-      } else {
-        for (int r = 0; r < a.RS; ++r) val += static_cast<double>(a.part[((size_t)r * a.T + t) * E + e]);
-        if (a.bias != nullptr) val += static_cast<double>(a.bias[e]);
-        if (a.logits_out != nullptr) a.logits_out[(size_t)t * E + e] = static_cast<float>(val);
-      }
-      if (val != val) nanmask |= 1u << i;
-    }
-    v[i] = val;
-  }
-
-  // Error bound of the fast logits (mode 1).
-  double bound = 0.0;
-  if (a.mode == 1) {
-    float sum = 0.f;
-    for (int r = 0; r < a.RS; ++r) {
-      float m = 0.f;
-      for (int c = lane; c < a.CS; c += kWave) m = fmaxf(m, a.amax[((size_t)r * a.CS + c) * a.T + t]);
-      sum += wave_max_f(m);
-    }
-    float bm = 0.f;
-    if (a.bias != nullptr)
-      for (int e = lane; e < E; e += kWave) bm = fmaxf(bm, fabsf(a.bias[e]));
-    sum += wave_max_f(bm);
-    bound = static_cast<double>(sum) * 0x1p-23;
-  }
-
-  uint32_t excluded = 0;  // lanes' experts not eligible (after a recompute)
-  // Lane r keeps the r-th selected (value, id, class).
-  double top_v = 0.0;
-  int top_i = 0, top_c = 0;
-  auto select = [&](int rounds) -> int {
-    uint32_t sel = 0;
-    int got = 0;
-    for (int r = 0; r < rounds; ++r) {
-      int bc = 0, bi = INT_MAX;
-      double bv = 0.0;
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i) {
-        const int e = lane + kWave * i;
-        if (e < E && !((sel >> i) & 1u) && !((excluded >> i) & 1u)) {
-          const int c = ((nanmask >> i) & 1u) ? 1 : 2;
-          if (better(c, v[i], e, bc, bv, bi)) {
-            bc = c;
-            bv = v[i];
-            bi = e;
-          }
-        }
-      }
-      for (int m = 32; m >= 1; m >>= 1) {
-        const int oc = __shfl_xor(bc, m, kWave);
-        const double ov = __shfl_xor(bv, m, kWave);
-        const int oi = __shfl_xor(bi, m, kWave);
-        if (better(oc, ov, oi, bc, bv, bi)) {
-          bc = oc;
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (bc == 0) break;
-      if ((bi & (kWave - 1)) == lane) sel |= 1u << (bi / kWave);
-      if (lane == r) {
-        top_v = bv;
-        top_i = bi;
-        top_c = bc;
-      }
-      ++got;
-    }
-    return got;
-  };
-
-  const int K1 = (k + 1 <= E) ? k + 1 : k;
-  const int got = select(a.mode == 1 ? K1 : k);
-
-  if (a.mode == 1) {
-    // Lane r < got-1 checks the gap between the r-th and (r+1)-th values.
-    const double next_v = __shfl_down(top_v, 1, kWave);
-    const bool fin_r = (lane >= got) || (top_c == 2 && (top_v - top_v == 0.0));
-    const bool finite = __all(fin_r);
-    const bool gap_ok = (lane + 1 >= got) || (top_v - next_v > 2.0 * bound);
-    const bool ok = (got == K1) && finite && __all(gap_ok);
-    if (a.recomputed != nullptr && lane == 0) a.recomputed[t] = ok ? 0 : 1;
-    if (!ok) {
-      // Every exact top-k member has a fast logit >= (k-th fast value) - 2*bound.
-      const double thr = __shfl(top_v, k - 1, kWave) - 2.0 * bound;
-      const uint16_t* xrow = a.x + (size_t)t * a.H;
-      for (int i = 0; i < kEPL; ++i) {
-        const int e = lane + kWave * i;
-        const bool cand = (e < E) && (!finite || (!((nanmask >> i) & 1u) && v[i] >= thr));
-        if (e < E && !cand) excluded |= 1u << i;
-        uint64_t mask = __ballot(cand);
-        while (mask) {
-          const int l = __builtin_ctzll(mask);
-          mask &= mask - 1;
-          const double val = dd_logit(xrow, a.wr, a.H, E, l + kWave * i, a.bias);
-          if (lane == l) {
-            v[i] = val;
-            if (val != val) nanmask |= 1u << i;
-            else nanmask &= ~(1u << i);
-          }
-        }
-      }
-      select(k);
-    }
-  }
-
-  // Weights: softmax over the k selected (renormalised) or over all E.
-  const double v0 = __shfl(top_v, 0, kWave);
-  double z = 0.0;
-  if (lane < k) z = exp(top_v - v0);
-  double denom;
-  if (a.renorm) {
-    denom = z;
-    for (int m = 32; m >= 1; m >>= 1) denom += __shfl_xor(denom, m, kWave);
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+  __shared__ BlockTopkSmem sm;
+  __shared__ float amax_w[kTopkThreads / kWave];
+  const int t = blockIdx.x, E = a.E;
+  if (a.mode == 0) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      sm.v[e] = static_cast<double>(a.part[(size_t)t * E + e]);
   } else {
-    double part = 0.0;
-#pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E) part += exp(v[i] - v0);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      double l = 0.0;
+      for (int r = 0; r < a.RS; ++r) l += static_cast<double>(a.part[((size_t)r * a.T + t) * E + e]);
+      if (a.bias != nullptr) l += static_cast<double>(a.bias[e]);
+      sm.v[e] = l;
+      if (a.logits_out != nullptr) a.logits_out[(size_t)t * E + e] = static_cast<float>(l);
     }
-    denom = part;
-    for (int m = 32; m >= 1; m >>= 1) denom += __shfl_xor(denom, m, kWave);
   }
-  if (lane < k) {
-    a.ids[(size_t)t * k + lane] = top_i;
-    a.w[(size_t)t * k + lane] = static_cast<float>(z / denom);
+  // Error bound of the fast logits (mode 1): 2^-23 * max_e sum|x||w| (+|b|).
+  float m = 0.f;
+  if (a.mode == 1) {
+    for (int i = threadIdx.x; i < a.RS * a.CS; i += blockDim.x) {
+      const int r = i / a.CS, c = i % a.CS;
+      m = fmaxf(m, a.amax[((size_t)r * a.CS + c) * a.T + t]);
+    }
+    if (a.bias != nullptr)
+      for (int e = threadIdx.x; e < E; e += blockDim.x) m = fmaxf(m, fabsf(a.bias[e]));
   }
+  m = wave_max_f(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) amax_w[threadIdx.x / kWave] = m;
+  __syncthreads();
+  float am = 0.f;
+  for (int i = 0; i < (int)(blockDim.x / kWave); ++i) am = fmaxf(am, amax_w[i]);
+  // With one slice (RS == 1) the max over column blocks is the max over
+  // experts; the bias term is added on top as a safe over-estimate.
+  BlockTopkArgs ta;
+  ta.E = E;
+  ta.k = a.k;
+  ta.renorm = a.renorm;
+  ta.bound = (a.mode == 1) ? static_cast<double>(am) * 2.0 * 0x1p-23 : 0.0;
+  ta.certify = a.mode == 1;
+  ta.xrow = a.x ? a.x + (size_t)t * a.H : nullptr;
+  ta.wr = a.wr;
+  ta.bias = a.bias;
+  ta.H = a.H;
+  ta.ids = a.ids + (size_t)t * a.k;
+  ta.w = a.w + (size_t)t * a.k;
+  block_topk(sm, ta);
 }
 
 }  // namespace
@@ -301,8 +158,7 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  dim3 grid((a.T + 3) / 4);
-  return launch(topk_kernel, grid, dim3(256), 0, s, a);
+  return launch(topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
 }
 
 }  // namespace moe

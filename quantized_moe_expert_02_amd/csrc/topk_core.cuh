@@ -1,0 +1,418 @@
+// Per-token top-k selection (one wavefront per token) and small-batch
+// grouping (one wavefront), shared by the standalone and fused kernels.
+//
+// Selection order: larger logit first, then lower expert id; NaN after every
+// number.  Routing is decided on the exact logit rounded once to float64: the
+// caller's fast logits come with a rigorous error bound, and when the bound
+// cannot separate two adjacent entries of the top k+1, the contested logits
+// are recomputed with a compensated float64 sum (products of a bf16 input and
+// an fp32 router weight are exact in float64).
+#pragma once
+#include <climits>
+
+#include "moe_device.cuh"
+
+namespace moe {
+
+// Selection key: class 2 = a number (incl. +-inf), 1 = NaN, 0 = not eligible.
+__device__ __forceinline__ bool key_better(int ca, double va, int ia, int cb, double vb, int ib) {
+  if (ca != cb) return ca > cb;
+  if (ca == 2 && va != vb) return va > vb;
+  return ia < ib;
+}
+
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& err) {
+  s = a + b;
+  const double bp = s - a;
+  const double ap = s - bp;
+  err = (a - ap) + (b - bp);
+}
+
+// Compensated float64 logit of expert e for one token (whole wave; every lane
+// returns the same value).
+__device__ inline double dd_logit(const uint16_t* __restrict__ xrow, const float* __restrict__ wr,
+                                  int H, int E, int e, const float* bias) {
+  const int lane = __lane_id();
+  double s = 0.0, c = 0.0;
+  for (int h = lane; h < H; h += kWave) {
+    const double p = static_cast<double>(bf16_to_f32(xrow[h])) *
+                     static_cast<double>(wr[(size_t)h * E + e]);
+    double err;
+    two_sum(s, p, s, err);
+    c += err;
+  }
+  // Pairwise combine: both lanes of a pair compute identical values.
+  for (int m = 1; m < kWave; m <<= 1) {
+    const double os = __shfl_xor(s, m, kWave);
+    const double oc = __shfl_xor(c, m, kWave);
+    double err;
+    two_sum(s, os, s, err);
+    c = (c + oc) + err;
+  }
+  if (bias != nullptr) {
+    double err;
+    two_sum(s, static_cast<double>(bias[e]), s, err);
+    c += err;
+  }
+  return s + c;
+}
+
+struct TopkToken {
+  double* vals;        // LDS, [E] logits of this token (may be overwritten)
+  int E, k, renorm;
+  double bound;        // error bound of vals (ignored when !certify)
+  bool certify;
+  const uint16_t* xrow;  // for the recompute (certify only)
+  const float* wr;
+  const float* bias;
+  int H;
+  int* ids;            // [k] out
+  float* w;            // [k] out
+  int* recomputed;     // out flag or nullptr
+};
+
+// Lanes r < rounds hold the r-th selected entry in (top_v, top_i, top_c).
+__device__ inline int wave_select(const double* vals, int E, uint32_t excl, int rounds,
+                                  double& top_v, int& top_i, int& top_c) {
+  const int lane = __lane_id();
+  const int nper = (E + kWave - 1) / kWave;
+  uint32_t sel = 0;  // bit i: expert lane + 64*i selected
+  int got = 0;
+  for (int r = 0; r < rounds; ++r) {
+    int bc = 0, bi = INT_MAX;
+    double bv = 0.0;
+    for (int i = 0; i < nper; ++i) {
+      const int e = lane + kWave * i;
+      if (e >= E || ((sel >> i) & 1u) || ((excl >> i) & 1u)) continue;
+      const double v = vals[e];
+      const int c = (v != v) ? 1 : 2;
+      if (key_better(c, v, e, bc, bv, bi)) {
+        bc = c;
+        bv = v;
+        bi = e;
+      }
+    }
+    for (int m = 32; m >= 1; m >>= 1) {
+      const int oc = __shfl_xor(bc, m, kWave);
+      const double ov = __shfl_xor(bv, m, kWave);
+      const int oi = __shfl_xor(bi, m, kWave);
+      if (key_better(oc, ov, oi, bc, bv, bi)) {
+        bc = oc;
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bc == 0) break;
+    if ((bi & (kWave - 1)) == lane) sel |= 1u << (bi / kWave);
+    if (lane == r) {
+      top_v = bv;
+      top_i = bi;
+      top_c = bc;
+    }
+    ++got;
+  }
+  return got;
+}
+
+// Select, certify (optionally recompute), and write ids and weights.
+__device__ inline void wave_topk(const TopkToken& a) {
+  const int lane = __lane_id();
+  const int E = a.E, k = a.k;
+  const int K1 = (k + 1 <= E) ? k + 1 : k;
+  double top_v = 0.0;
+  int top_i = 0, top_c = 0;
+  uint32_t excl = 0;  // bit i: expert lane + 64*i not eligible (after a recompute)
+  int got = wave_select(a.vals, E, 0u, a.certify ? K1 : k, top_v, top_i, top_c);
+  if (a.certify) {
+    const double next_v = __shfl_down(top_v, 1, kWave);
+    const bool fin_r = (lane >= got) || (top_c == 2 && (top_v - top_v == 0.0));
+    const bool finite = __all(fin_r);
+    const bool gap_ok = (lane + 1 >= got) || (top_v - next_v > 2.0 * a.bound);
+    const bool ok = (got == K1) && finite && __all(gap_ok);
+    if (a.recomputed != nullptr && lane == 0) *a.recomputed = ok ? 0 : 1;
+    if (!ok) {
+      // Every exact top-k member has a fast logit >= (k-th fast value) - 2*bound.
+      const double thr = __shfl(top_v, k - 1, kWave) - 2.0 * a.bound;
+      const int nper = (E + kWave - 1) / kWave;
+      for (int i = 0; i < nper; ++i) {
+        const int e = lane + kWave * i;
+        const double v = (e < E) ? a.vals[e] : 0.0;
+        const bool cand = (e < E) && (!finite || (v == v && v >= thr));
+        if (e < E && !cand) excl |= 1u << i;
+        uint64_t mask = __ballot(cand);
+        while (mask) {
+          const int l = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          const double val = dd_logit(a.xrow, a.wr, a.H, E, l + kWave * i, a.bias);
+          if (lane == 0) a.vals[l + kWave * i] = val;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      got = wave_select(a.vals, E, excl, k, top_v, top_i, top_c);
+    }
+  }
+  // Weights: softmax over the k selected (renormalised) or over all E.
+  const double v0 = __shfl(top_v, 0, kWave);
+  double z = (lane < k) ? exp(top_v - v0) : 0.0;
+  double denom;
+  if (a.renorm) {
+    denom = z;
+  } else {
+    denom = 0.0;
+    for (int e = lane; e < E; e += kWave) denom += exp(a.vals[e] - v0);
+  }
+  for (int m = 32; m >= 1; m >>= 1) denom += __shfl_xor(denom, m, kWave);
+  if (lane < k) {
+    a.ids[lane] = top_i;
+    a.w[lane] = static_cast<float>(z / denom);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide top-k of one token by rank counting: each thread ranks its own
+// experts against all others (stopping once k+1 better ones are found), so
+// there is no serial round per selected expert.
+// ---------------------------------------------------------------------------
+constexpr int kTopkThreads = 512;
+
+struct BlockTopkSmem {
+  double v[kMaxExperts];            // logits of the token
+  uint64_t key[kMaxExperts];        // order keys (larger = better)
+  unsigned char excl[kMaxExperts];  // 1: not eligible (after a recompute)
+  double topv[kMaxTopK + 1];
+  int topi[kMaxTopK + 1];
+  int topc[kMaxTopK + 1];
+  int cand[kMaxExperts];
+  uint64_t ckey[kMaxExperts];
+  double dred[kTopkThreads / kWave];
+  int ncand;
+};
+
+// Unsigned order key of a logit: larger key = ranks earlier.  0 = not
+// eligible, 1 = NaN (after every number), numbers in IEEE order with -0 == +0.
+__device__ __forceinline__ uint64_t order_key(double v, bool excluded) {
+  if (excluded) return 0ull;
+  if (v != v) return 1ull;
+  if (v == 0.0) v = 0.0;
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// f ranks before e: larger key, or equal key and lower expert id.
+__device__ __forceinline__ int ranks_before(uint64_t kf, int f, uint64_t ke, int e) {
+  return (kf > ke) | ((kf == ke) & (f < e));
+}
+
+// Writes the first `rounds` entries of the order into topv/topi/topc.  Two
+// levels: the rank of each expert among the 64 of its chunk, then the rank of
+// the chunk-level survivors (rank < rounds) among themselves; every member of
+// the overall first `rounds` survives its chunk, and its rank among the
+// survivors is its overall rank.
+__device__ inline void block_rank(BlockTopkSmem& sm, int E, int rounds) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) sm.key[e] = order_key(sm.v[e], sm.excl[e] != 0);
+  if (threadIdx.x == 0) sm.ncand = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const uint64_t ke = sm.key[e];
+    const int c0 = e & ~(kWave - 1);
+    const int nf = min(kWave, E - c0);
+    int cnt = 0;
+#pragma unroll 16
+    for (int j = 0; j < kWave; ++j) {
+      const int f = c0 + j;
+      const uint64_t kf = sm.key[c0 + (j < nf ? j : 0)];
+      cnt += (j < nf) ? ranks_before(kf, f, ke, e) : 0;
+    }
+    if (ke != 0ull && cnt < rounds) {
+      const int slot = atomicAdd(&sm.ncand, 1);
+      sm.cand[slot] = e;
+      sm.ckey[slot] = ke;
+    }
+  }
+  __syncthreads();
+  const int nc = sm.ncand;
+  for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+    const int e = sm.cand[i];
+    const uint64_t ke = sm.ckey[i];
+    int cnt = 0;
+    for (int j = 0; j < nc; ++j) cnt += ranks_before(sm.ckey[j], sm.cand[j], ke, e);
+    if (cnt < rounds) {
+      sm.topv[cnt] = sm.v[e];
+      sm.topi[cnt] = e;
+      sm.topc[cnt] = (ke == 1ull) ? 1 : 2;
+    }
+  }
+}
+
+struct BlockTopkArgs {
+  int E, k, renorm;
+  double bound;  // error bound of the logits (used when certify)
+  bool certify;
+  const uint16_t* xrow;
+  const float* wr;
+  const float* bias;
+  int H;
+  int* ids;  // [k]
+  float* w;  // [k]
+};
+
+// sm.v must hold the token's logits and be visible to the whole block.
+__device__ inline void block_topk(BlockTopkSmem& sm, const BlockTopkArgs& a) {
+  const int E = a.E, k = a.k;
+  const int K1 = (k + 1 <= E) ? k + 1 : k;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) sm.excl[e] = 0;
+  __syncthreads();
+  block_rank(sm, E, a.certify ? K1 : k);
+  __syncthreads();
+  if (a.certify) {
+    int bad = 0;
+    if ((int)threadIdx.x < K1) {
+      const int r = threadIdx.x;
+      const double vr = sm.topv[r];
+      if (sm.topc[r] != 2 || !(vr - vr == 0.0)) bad = 2;  // non-finite or NaN among the top k+1
+      else if (r + 1 < K1 && !(vr - sm.topv[r + 1] > 2.0 * a.bound)) bad = 1;
+    }
+    const int any_bad = __syncthreads_or(bad);
+    if (any_bad) {
+      const int all = __syncthreads_or(bad == 2);
+      // Every exact top-k member has a fast logit >= (k-th fast value) - 2*bound.
+      const double thr = sm.topv[k - 1] - 2.0 * a.bound;
+      if (threadIdx.x == 0) sm.ncand = 0;
+      __syncthreads();
+      for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const double v = sm.v[e];
+        const bool cand = all || (v == v && v >= thr);
+        if (cand) sm.cand[atomicAdd(&sm.ncand, 1)] = e;
+        else sm.excl[e] = 1;
+      }
+      __syncthreads();
+      for (int i = wave; i < sm.ncand; i += nwaves) {
+        const int c = sm.cand[i];
+        const double val = dd_logit(a.xrow, a.wr, a.H, E, c, a.bias);
+        if (lane == 0) sm.v[c] = val;
+      }
+      __syncthreads();
+      block_rank(sm, E, k);
+      __syncthreads();
+    }
+  }
+  // Weights: softmax over the k selected (renormalised) or over all E.
+  const double v0 = sm.topv[0];
+  if (!a.renorm) {
+    double part = 0.0;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) part += exp(sm.v[e] - v0);
+    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
+    if (lane == 0) sm.dred[wave] = part;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const double z = (lane < k) ? exp(sm.topv[lane] - v0) : 0.0;
+    double denom = 0.0;
+    if (a.renorm) {
+      denom = z;
+      for (int m = 32; m >= 1; m >>= 1) denom += __shfl_xor(denom, m, kWave);
+    } else {
+      for (int i = 0; i < nwaves; ++i) denom += sm.dred[i];
+    }
+    if (lane < k) {
+      a.ids[lane] = sm.topi[lane];
+      a.w[lane] = static_cast<float>(z / denom);
+    }
+  }
+}
+
+// Per-group descriptor the fused decode kernels read in one step.
+constexpr int kGroupDescInts = 20;  // e, p0, nrows, spare, 16 input-token rows
+constexpr int kGroupDescRows = 16;
+
+// Stable counting sort of P pairs by expert id, by one wavefront.
+//   cnt, aidx, off0: LDS scratch [E].  active: [E+1] (count, then ids).
+//   desc (optional): [E][kGroupDescInts] group descriptors in active order;
+//   the token list holds pair/topk for the first kGroupDescRows rows.
+__device__ inline void wave_group(const int* ids, int P, int E, int topk, int* counts,
+                                  int* offsets, int* perm_to_pair, int* pair_to_perm, int* active,
+                                  int* desc, int* cnt, int* aidx, int* off0) {
+  const int lane = __lane_id();
+  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  for (int p = lane; p < P; p += kWave) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  // offsets (exclusive scan) and the active list, 64 experts at a time
+  int run = 0, nact = 0;
+  for (int base = 0; base < E; base += kWave) {
+    const int e = base + lane;
+    const int c = (e < E) ? cnt[e] : 0;
+    int x = c;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(x, d, kWave);
+      if (lane >= d) x += y;
+    }
+    const int excl_off = run + x - c;
+    const uint64_t nz = __ballot(c > 0);
+    const int arank = __popcll(nz & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+    if (e < E) {
+      if (counts != nullptr) counts[e] = c;
+      offsets[e] = excl_off;
+      cnt[e] = excl_off;  // next free position of expert e
+      off0[e] = excl_off;
+      aidx[e] = (c > 0) ? nact + arank : -1;
+      if (c > 0) {
+        active[1 + nact + arank] = e;
+        if (desc != nullptr) {
+          int* d = desc + (size_t)(nact + arank) * kGroupDescInts;
+          d[0] = e;
+          d[1] = excl_off;
+          d[2] = c;
+          d[3] = 0;
+        }
+      }
+    }
+    run += __shfl(x, kWave - 1, kWave);
+    nact += __popcll(nz);
+  }
+  if (lane == 0) {
+    offsets[E] = run;
+    active[0] = nact;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s = 0; s < P; s += kWave) {
+    const int p = s + lane;
+    const int e0 = (p < P) ? ids[p] : -1;
+    const bool valid = (p < P) && (unsigned)e0 < (unsigned)E;
+    const int e = valid ? e0 : 0;
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t m = __ballot(valid && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? m : ~m;
+    }
+    const int pos = valid ? cnt[e] + __popcll(same & lt) : 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      perm_to_pair[pos] = p;
+      pair_to_perm[p] = pos;
+      if (desc != nullptr) {
+        const int u = aidx[e];
+        const int r = pos - off0[e];
+        if (u >= 0 && r < kGroupDescRows) desc[(size_t)u * kGroupDescInts + 4 + r] = p / topk;
+      }
+      if ((same >> lane) == 1ull) cnt[e] = pos + 1;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace moe

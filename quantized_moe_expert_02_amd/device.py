@@ -83,7 +83,7 @@ class DeviceLayer:
         n = _lib.moe_workspace_size(self.desc, T)
         if n == 0:
             raise _lib.MoeError(_lib.MOE_ERR_INVALID_ARG, "moe_workspace_size")
-        return torch.empty(n, dtype=torch.uint8, device=self.device)
+        return torch.zeros(n, dtype=torch.uint8, device=self.device)  # zero-filled once
 
 
 def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:

@@ -109,12 +109,12 @@ def test_entry_points_reject_before_any_launch():
     assert moe.moe_layer_forward(L, FAKE, -1, FAKE, FAKE, 0, check=False) == moe.MOE_ERR_INVALID_ARG
     assert moe.moe_route_topk(L, FAKE, FAKE, 4, FAKE, FAKE, None, 0, check=False) == moe.MOE_ERR_WORKSPACE
     assert moe.moe_route_topk(L, None, None, 4, FAKE, FAKE, None, 0, check=False) == moe.MOE_ERR_INVALID_ARG
-    assert moe.moe_permute(FAKE, 4, 11, 10, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, check=False) == -1
-    assert moe.moe_permute(FAKE, 4, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, 8, check=False) == -3
+    assert moe.moe_permute(FAKE, 4, 11, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, check=False) == -1
+    assert moe.moe_permute(FAKE, 4, 2, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, check=False) == -3
     assert moe.moe_combine(FAKE, FAKE, FAKE, None, 4, 2, 2050, FAKE, check=False) == -2
-    assert moe.moe_expert_gemm(7, L, 0, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 1 << 40, check=False) == -1
+    assert moe.moe_expert_gemm(7, L, 0, FAKE, FAKE, None, 4, FAKE, FAKE, FAKE, 1 << 40, check=False) == -1
     L.has_shared = 0
-    assert moe.moe_expert_gemm(0, L, 1, None, None, 4, FAKE, FAKE, None, 0, check=False) == -1
+    assert moe.moe_expert_gemm(0, L, 1, None, None, None, 4, FAKE, FAKE, None, 0, check=False) == -1
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
