@@ -14,9 +14,10 @@
 //   2. one block per token: sum the slices, select the top-k by rank counting,
 //      certify it against the exact logits (recomputing near ties), weights;
 //   3. each active routed expert's gate/up + SwiGLU, its weights streamed once
-//      for all of its tokens (each block derives its expert and (token, slot)
-//      pairs from the <= 256 routed ids); extra blocks run the shared
-//      expert's down projection;
+//      for all of its tokens (blocks are laid out per routed pair slot; the
+//      block of an expert's first pair derives the expert's (token, slot)
+//      pairs from the <= 256 routed ids, the others exit); extra blocks run
+//      the shared expert's down projection;
 //   4. each active expert's down projection;
 //   5. combine: per-expert partials in fp32, in slot order, then the shared
 //      expert, rounded once to bf16.
@@ -165,63 +166,42 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a)
   block_topk(sm, ta);
 }
 
-// Expert group u (the u-th smallest routed expert id) and its (token, slot)
-// pairs in increasing pair order.  Block-wide; returns false when fewer than
-// u+1 experts are active.
+// Expert group of pair slot q: the expert e = ids[q] and all (token, slot)
+// pairs routed to it, in pair order.  Only the first pair of each expert
+// proceeds (returns false for the others), so every active expert is
+// processed exactly once.  Block-wide, two barriers.
 struct GroupSmem {
-  int ids[kPmax];
-  unsigned bits[kMaxExperts / 32];
-  int wcnt[4];
   int pairs[kPmax];
   int toks[kPmax];
-  int e, n;
+  int wcnt[4];
+  int wdup[4];
 };
 
-__device__ inline bool derive_group(const DecodeArgs& a, int u, GroupSmem& g) {
-  const int P = a.T * a.k, E = a.E;
-  const int nw = (E + 31) / 32;
+__device__ inline bool derive_group(const DecodeArgs& a, int q, GroupSmem& g, int& e_out, int& n_out) {
+  const int P = a.T * a.k;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  for (int p = threadIdx.x; p < P; p += blockDim.x) g.ids[p] = a.ids[p];
-  for (int i = threadIdx.x; i < nw; i += blockDim.x) g.bits[i] = 0u;
-  __syncthreads();
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    const int e = g.ids[p];
-    if ((unsigned)e < (unsigned)E) atomicOr(&g.bits[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
-  if (wave == 0) {
-    if (lane == 0) g.e = -1;
-    const unsigned b = (lane < nw) ? g.bits[lane] : 0u;
-    const int c = __popc(b);
-    int incl = c;
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int y = __shfl_up(incl, d, kWave);
-      if (lane >= d) incl += y;
-    }
-    const int excl = incl - c;
-    if (lane < nw && excl <= u && u < incl) {
-      unsigned bb = b;
-      for (int i = 0; i < u - excl; ++i) bb &= bb - 1u;
-      g.e = lane * 32 + __builtin_ctz(bb);
-    }
-  }
-  __syncthreads();
-  const int e = g.e;
-  if (e < 0) return false;
-  // pairs of expert e, in pair order (P <= 256 = one pass of 256 threads)
-  const int p = threadIdx.x;
-  const bool m = (p < P) && g.ids[p] == e;
+  const int e = a.ids[q];
+  const int j = threadIdx.x;  // P <= 256 = blockDim
+  const int my = (j < P) ? a.ids[j] : -1;
+  const bool m = (j < P) && my == e;
   const uint64_t bal = __ballot(m);
-  if (lane == 0) g.wcnt[wave] = __popcll(bal);
+  const uint64_t dup = __ballot(m && j < q);
+  if (lane == 0) {
+    g.wcnt[wave] = __popcll(bal);
+    g.wdup[wave] = dup != 0ull;
+  }
   __syncthreads();
+  if (g.wdup[0] | g.wdup[1] | g.wdup[2] | g.wdup[3]) return false;
+  if ((unsigned)e >= (unsigned)a.E) return false;
   int base = 0;
   for (int w = 0; w < wave; ++w) base += g.wcnt[w];
   if (m) {
     const int pos = base + __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-    g.pairs[pos] = p;
-    g.toks[pos] = p / a.k;
+    g.pairs[pos] = j;
+    g.toks[pos] = j / a.k;
   }
-  if (threadIdx.x == 0) g.n = g.wcnt[0] + g.wcnt[1] + g.wcnt[2] + g.wcnt[3];
+  e_out = e;
+  n_out = g.wcnt[0] + g.wcnt[1] + g.wcnt[2] + g.wcnt[3];
   __syncthreads();
   return true;
 }
@@ -234,13 +214,14 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DecodeArgs a) {
   } sm;
   __shared__ GroupSmem grp;
   const int ntiles = a.I / gemv_rows_per_block<kOpGateUp>();
-  const int nrouted = a.max_groups * ntiles;
+  const int nrouted = a.T * a.k * ntiles;
   if ((int)blockIdx.x < nrouted) {
-    const int u = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
-    if (!derive_group(a, u, grp)) return;
+    const int q = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+    int e, n;
+    if (!derive_group(a, q, grp, e, n)) return;
     GemvIO io{a.x, a.h, nullptr, a.k, kInList, a.T};
-    gemv_tile<RFMT, kOpGateUp, 1, 4>(a.gate, a.up, io, GemvRows{grp.e, 0, grp.n, grp.toks, grp.pairs},
-                                     tile, sm.g);
+    gemv_tile<RFMT, kOpGateUp, 1, 4>(a.gate, a.up, io, GemvRows{e, 0, n, grp.toks, grp.pairs}, tile,
+                                     sm.g);
   } else if constexpr (SFMT != 0) {  // shared expert down projection
     GemvIO io{a.hs, a.ys, nullptr, a.k, kInShared, a.T};
     gemv_tile<SFMT, kOpDown, 4, 1>(a.sd, a.sd, io, GemvRows{0, 0, a.T, nullptr, nullptr},
@@ -254,11 +235,12 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeArgs a) {
   __shared__ GroupSmem grp;
   constexpr int RPB = gemv_rows_per_block<kOpDown>();
   const int ntiles = (a.H + RPB - 1) / RPB;
-  const int u = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
-  if (!derive_group(a, u, grp)) return;
+  const int q = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+  int e, n;
+  if (!derive_group(a, q, grp, e, n)) return;
   GemvIO io{a.h, a.y, nullptr, a.k, kInList, a.T * a.k};
-  gemv_tile<RFMT, kOpDown, 4, 1>(a.down, a.down, io, GemvRows{grp.e, 0, grp.n, grp.pairs, grp.pairs},
-                                 tile, sm);
+  gemv_tile<RFMT, kOpDown, 4, 1>(a.down, a.down, io, GemvRows{e, 0, n, grp.pairs, grp.pairs}, tile,
+                                 sm);
 }
 
 // out[t] = bf16( sum_j w[t,j] * y[t*k+j] + y_shared[t] ), four columns per thread.
@@ -300,11 +282,11 @@ hipError_t launch5(const DecodeArgs& a, hipStream_t s) {
   err = launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
   if (err != hipSuccess) return err;
   constexpr int RPD = gemv_rows_per_block<kOpDown>();
-  const int ngu = a.max_groups * (a.I / gemv_rows_per_block<kOpGateUp>());
+  const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
   const int nsd = (SFMT != 0) ? (a.H + RPD - 1) / RPD : 0;
   err = launch(decode_gateup_kernel<RFMT, SFMT>, dim3(ngu + nsd), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
-  const int nd = a.max_groups * ((a.H + RPD - 1) / RPD);
+  const int nd = a.T * a.k * ((a.H + RPD - 1) / RPD);
   err = launch(decode_down_kernel<RFMT>, dim3(nd), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
   return launch(decode_combine_kernel, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, s, a);

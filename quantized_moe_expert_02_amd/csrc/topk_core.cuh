@@ -178,13 +178,13 @@ constexpr int kTopkThreads = 512;
 
 struct BlockTopkSmem {
   double v[kMaxExperts];            // logits of the token
-  uint64_t key[kMaxExperts];        // order keys (larger = better)
   unsigned char excl[kMaxExperts];  // 1: not eligible (after a recompute)
   double topv[kMaxTopK + 1];
   int topi[kMaxTopK + 1];
   int topc[kMaxTopK + 1];
   int cand[kMaxExperts];
   uint64_t ckey[kMaxExperts];
+  int crank[kMaxExperts];
   double dred[kTopkThreads / kWave];
   int ncand;
 };
@@ -205,42 +205,57 @@ __device__ __forceinline__ int ranks_before(uint64_t kf, int f, uint64_t ke, int
 }
 
 // Writes the first `rounds` entries of the order into topv/topi/topc.  Two
-// levels: the rank of each expert among the 64 of its chunk, then the rank of
-// the chunk-level survivors (rank < rounds) among themselves; every member of
-// the overall first `rounds` survives its chunk, and its rank among the
-// survivors is its overall rank.
+// levels: the rank of each expert among the 64 of its wavefront (keys
+// broadcast from registers with v_readlane), then the rank of the
+// wavefront-level survivors (rank < rounds) among themselves, the comparisons
+// split across the whole block.  Every member of the overall first `rounds`
+// survives its wavefront, and its rank among the survivors is its overall rank.
 __device__ inline void block_rank(BlockTopkSmem& sm, int E, int rounds) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) sm.key[e] = order_key(sm.v[e], sm.excl[e] != 0);
   if (threadIdx.x == 0) sm.ncand = 0;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const uint64_t ke = sm.key[e];
-    const int c0 = e & ~(kWave - 1);
-    const int nf = min(kWave, E - c0);
+  for (int base = 0; base < E; base += blockDim.x) {
+    const int e = base + threadIdx.x;
+    const bool valid = e < E;
+    const uint64_t ke = valid ? order_key(sm.v[e], sm.excl[e] != 0) : 0ull;
+    const uint32_t klo = static_cast<uint32_t>(ke), khi = static_cast<uint32_t>(ke >> 32);
+    const int f0 = e & ~(kWave - 1);
     int cnt = 0;
 #pragma unroll 16
-    for (int j = 0; j < kWave; ++j) {
-      const int f = c0 + j;
-      const uint64_t kf = sm.key[c0 + (j < nf ? j : 0)];
-      cnt += (j < nf) ? ranks_before(kf, f, ke, e) : 0;
+    for (int i = 0; i < kWave; ++i) {
+      // readlane returns int: widen through uint32_t (no sign extension)
+      const uint64_t ki =
+          (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(khi, i))) << 32) |
+          static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(klo, i)));
+      cnt += ranks_before(ki, f0 + i, ke, e);
     }
-    if (ke != 0ull && cnt < rounds) {
+    if (valid && ke != 0ull && cnt < rounds) {
       const int slot = atomicAdd(&sm.ncand, 1);
       sm.cand[slot] = e;
       sm.ckey[slot] = ke;
+      sm.crank[slot] = 0;
     }
   }
   __syncthreads();
   const int nc = sm.ncand;
-  for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+  const int segs = max(1, (int)blockDim.x / max(nc, 1));
+  const int len = (nc + segs - 1) / segs;
+  if ((int)threadIdx.x < nc * segs) {
+    const int i = threadIdx.x % nc, sgm = threadIdx.x / nc;
     const int e = sm.cand[i];
     const uint64_t ke = sm.ckey[i];
+    const int j1 = min(nc, (sgm + 1) * len);
     int cnt = 0;
-    for (int j = 0; j < nc; ++j) cnt += ranks_before(sm.ckey[j], sm.cand[j], ke, e);
-    if (cnt < rounds) {
-      sm.topv[cnt] = sm.v[e];
-      sm.topi[cnt] = e;
-      sm.topc[cnt] = (ke == 1ull) ? 1 : 2;
+    for (int j = sgm * len; j < j1; ++j) cnt += ranks_before(sm.ckey[j], sm.cand[j], ke, e);
+    if (cnt) atomicAdd(&sm.crank[i], cnt);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+    const int r = sm.crank[i];
+    if (r < rounds) {
+      const int e = sm.cand[i];
+      sm.topv[r] = sm.v[e];
+      sm.topi[r] = e;
+      sm.topc[r] = (sm.ckey[i] == 1ull) ? 1 : 2;
     }
   }
 }
