@@ -15,8 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "expert_gemv.hip", "decode.hip",
-           "combine.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "expert_gemv.hip", "expert_gemm.hip",
+           "decode.hip", "combine.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
@@ -43,7 +43,10 @@ def _run(cmd):
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    missing = [s for s in SOURCES if not os.path.exists(os.path.join(CSRC, s))]
+    if missing:
+        raise RuntimeError("missing sources: " + ", ".join(missing))
+    srcs = SOURCES
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))

@@ -1,0 +1,363 @@
+// Prefill grouped expert GEMM (row groups larger than a decode batch).
+//
+// The pages run prefill expert GEMMs "over a compact list of the routed
+// segments' tiles instead of a grid over the longest segment" and run the gate
+// and up projections in one launch (gitee "dgpp" README, "Execution and
+// performance", engine.expert_tile_list and engine.expert_gemm_pair).  Here:
+//
+// * one workgroup (4 wavefronts) computes a 128-row tile of one expert's group
+//   (rows = permuted (token, slot) pairs) against 128 weight rows: for
+//   gate/up, 64 gate rows and the matching 64 up rows (SwiGLU in the
+//   epilogue, 64 h columns out); for down, 128 output columns;
+// * K advances 64 at a time; the weight tile is decoded once per step from its
+//   checkpoint format into bf16 in LDS (NVFP4: E2M1 x E4M3, exact in bf16;
+//   MXFP4: E2M1 x E8M0; FP8: E4M3, with each 128x128 block scale applied to the
+//   partial sum of its K block) and shared by all 128 rows; activations are
+//   gathered into LDS; both are double-buffered in registers across steps;
+// * each wavefront computes a 64x64 sub-tile with v_mfma_f32_16x16x32_bf16
+//   (bf16 products exact in fp32, fp32 accumulation);
+// * blocks are ordered so that every column tile of one row tile lands on the
+//   same XCD (its activation rows stay in that XCD's L2).
+#include "gemv_core.cuh"
+
+namespace moe {
+namespace {
+
+constexpr int BM = kGemmTileM, BN = 128, BK = 64;
+constexpr int LDSW = BK + 8;  // padded row (bf16 elements): 144-byte rows spread the banks
+constexpr int kXcds = 8;
+
+struct GemmParams {
+  WDesc w0, w1;           // gate, up (gate/up) or down (both)
+  const uint16_t* in;     // x [T][H] (gate/up) or h [rows][I] (down)
+  void* out;              // h bf16 [rows][I] or y fp32 [rows][H]
+  const int2* tiles;      // (expert, first permuted row) per row tile; nullptr: shared expert
+  const int* n_tiles;
+  const int* offsets;     // [E+1] group bounds (routed)
+  const int* perm_to_pair;
+  int topk;
+  int T;                  // shared expert rows
+  int in_rows;            // rows of `in`
+  int in_rows_total;      // permuted rows (T*k)
+  int max_rt;             // row tiles the grid was sized for
+  int ntn;                // column tiles
+};
+
+struct GemmSmem {
+  uint16_t a[2][BM][LDSW];
+  uint16_t b[2][BN][LDSW];
+};
+
+// Per-thread staging of one K step: 32 activations and 32 weights.
+template <int FMT>
+struct Stage {
+  u32x4 a[4];   // 32 bf16 activations
+  u32x4 q[2];   // FP4: q[0] = 32 codes; FP8: q[0..1] = 32 codes
+  uint32_t s;   // NVFP4: two E4M3 scales; MXFP4: one E8M0
+};
+
+template <int FMT>
+__device__ __forceinline__ void decode32(const Stage<FMT>& st, uint32_t (&w)[16]) {
+  if constexpr (FMT == FMT_NVFP4) {
+    const f32x2 sc = e4m3x2_to_f32(st.s);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float s = (d < 2) ? sc[0] : sc[1];
+      const uint32_t v = st.q[0][d];
+      const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
+      const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
+      const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
+      const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
+      w[4 * d + 0] = pack_hi16(f0[0] * s, f0[1] * s);
+      w[4 * d + 1] = pack_hi16(f1[0] * s, f1[1] * s);
+      w[4 * d + 2] = pack_hi16(f2[0] * s, f2[1] * s);
+      w[4 * d + 3] = pack_hi16(f3[0] * s, f3[1] * s);
+    }
+  } else if constexpr (FMT == FMT_MXFP4) {
+    const float s = __uint_as_float(st.s << 23);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t v = st.q[0][d];
+      union {
+        bf16x2 h;
+        uint32_t u;
+      } c0, c1, c2, c3;
+      c0.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0);
+      c1.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1);
+      c2.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2);
+      c3.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3);
+      w[4 * d + 0] = c0.u;
+      w[4 * d + 1] = c1.u;
+      w[4 * d + 2] = c2.u;
+      w[4 * d + 3] = c3.u;
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t v = st.q[d / 4][d % 4];
+      union {
+        bf16x2 h;
+        uint32_t u;
+      } c0, c1;
+      c0.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
+      c1.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true);
+      w[2 * d + 0] = c0.u;
+      w[2 * d + 1] = c1.u;
+    }
+  }
+}
+
+template <int FMT, int OP>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
+  __shared__ GemmSmem sm;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // XCD-aware order: workgroup b runs on XCD b % 8.  Each XCD takes a
+  // contiguous range of the live (row tile, column tile) pairs, column tiles
+  // fastest, so the column tiles of one row tile (same activation rows) and
+  // the row tiles of one expert (same weights) share that XCD's L2.
+  const int n_rt = (p.tiles == nullptr) ? (p.T + BM - 1) / BM : min(*p.n_tiles, p.max_rt);
+  const int live = n_rt * p.ntn;
+  const int per = (live + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int idx = xcd * per + local;
+  if (local >= per || idx >= live) return;
+  const int mt = idx / p.ntn, nt = idx % p.ntn;
+  int e, m0, m1;
+  if (p.tiles == nullptr) {  // shared expert over rows 0..T-1
+    e = 0;
+    m0 = mt * BM;
+    m1 = p.T;
+  } else {
+    const int2 tl = p.tiles[mt];
+    e = tl.x;
+    m0 = tl.y;
+    m1 = p.offsets[e + 1];
+    if (m0 < 0 || m1 > p.in_rows_total || m0 >= m1) return;
+  }
+  const int N = p.w0.rows, K = p.w0.cols;
+  const int n0 = nt * ((OP == kOpGateUp) ? BN / 2 : BN);  // first weight row of this tile
+
+  // ---- staging roles: thread -> (tile row, K half) ----
+  const int srow = tid >> 1, shalf = tid & 1;
+  // activation row
+  const uint16_t* arow = nullptr;
+  {
+    const int pr = m0 + srow;
+    if (pr < m1) {
+      int ir;
+      if (p.tiles == nullptr)
+        ir = pr;
+      else if (OP == kOpGateUp)
+        ir = p.perm_to_pair[pr] / p.topk;
+      else
+        ir = pr;
+      if ((unsigned)ir < (unsigned)p.in_rows) arow = p.in + (size_t)ir * K;
+    }
+  }
+  // weight row: gate/up tiles hold 64 gate rows then the matching 64 up rows
+  const WDesc& wq = (OP == kOpGateUp && srow >= BN / 2) ? p.w1 : p.w0;
+  const int wr = (OP == kOpGateUp) ? n0 + (srow & (BN / 2 - 1)) : n0 + srow;
+  const bool wvalid = wr < N;
+  const int rb = row_bytes<FMT>(K);
+  const uint8_t* wrow = wvalid ? wq.codes + e * wq.stride_codes + (size_t)wr * rb : nullptr;
+  const uint8_t* wsrow = wvalid ? scale_row_ptr<FMT>(wq, e, wr) : nullptr;
+
+  auto load_stage = [&](int k0, Stage<FMT>& st) {
+    const int kb = k0 + 32 * shalf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = kb + 8 * i;
+      st.a[i] = (arow != nullptr && k < K) ? *reinterpret_cast<const u32x4*>(arow + k)
+                                           : u32x4{0, 0, 0, 0};
+    }
+    st.q[0] = u32x4{0, 0, 0, 0};
+    st.q[1] = u32x4{0, 0, 0, 0};
+    st.s = 0;
+    if (wrow != nullptr && kb < K) {
+      if constexpr (FMT == FMT_FP8) {
+        st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb);
+        if (kb + 16 < K) st.q[1] = *reinterpret_cast<const u32x4*>(wrow + kb + 16);
+      } else {
+        st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb / 2);
+        if constexpr (FMT == FMT_NVFP4)
+          st.s = *reinterpret_cast<const uint16_t*>(wsrow + kb / 16);
+        else
+          st.s = wsrow[kb / 32];
+      }
+    }
+  };
+  auto store_stage = [&](int buf, const Stage<FMT>& st) {
+    uint16_t* ad = &sm.a[buf][srow][32 * shalf];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(ad + 8 * i) = st.a[i];
+    uint32_t w[16];
+    decode32<FMT>(st, w);
+    uint16_t* bd = &sm.b[buf][srow][32 * shalf];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(bd + 8 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+  };
+
+  // ---- MFMA roles: wave (wm, wn) owns rows [64wm, +64) and four 16-wide
+  // column tiles: down -> B rows 64wn + 16c; gate/up -> gate rows 32wn + 16c
+  // (c = 0,1) and the matching up rows 64 + 32wn + 16c (c = 2,3).
+  const int wm = wave >> 1, wn = wave & 1;
+  int bcol[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    bcol[c] = (OP == kOpGateUp) ? ((c < 2) ? 32 * wn + 16 * c : 64 + 32 * wn + 16 * (c - 2))
+                                : 64 * wn + 16 * c;
+  f32x4 acc[4][4];
+  f32x4 tmp[4][4];  // FP8: the current 128-wide K block
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tmp[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int nk = (K + BK - 1) / BK;
+  Stage<FMT> st;
+  load_stage(0, st);
+  store_stage(0, st);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    const bool more = ks + 1 < nk;
+    if (more) load_stage((ks + 1) * BK, st);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8 af[4], bfr[4];
+      const int ko = kk + 8 * (lane >> 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        af[r] = *reinterpret_cast<const bf16x8*>(&sm.a[buf][64 * wm + 16 * r + (lane & 15)][ko]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        bfr[c] = *reinterpret_cast<const bf16x8*>(&sm.b[buf][bcol[c] + (lane & 15)][ko]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if constexpr (FMT == FMT_FP8)
+            tmp[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[c], tmp[r][c], 0, 0, 0);
+          else
+            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[c], acc[r][c], 0, 0, 0);
+        }
+    }
+    if constexpr (FMT == FMT_FP8) {
+      // close a 128-wide K block: acc += s(block) * partial
+      const int kend = (ks + 1) * BK;
+      if ((kend % 128) == 0 || !more) {
+        const int kblk = (ks * BK) / 128;
+        const int cb = (K + 127) / 128;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const WDesc& wc = (OP == kOpGateUp && c >= 2) ? p.w1 : p.w0;
+          const int row = n0 + ((OP == kOpGateUp) ? (bcol[c] & (BN / 2 - 1)) : bcol[c]);
+          float s = 0.f;
+          if (row < N) {
+            const float* sp = reinterpret_cast<const float*>(
+                reinterpret_cast<const uint8_t*>(wc.scales) + e * wc.stride_scales);
+            s = sp[(size_t)(row / 128) * cb + kblk];
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[r][c] = acc[r][c] + s * tmp[r][c];
+            tmp[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+      }
+    }
+    if (more) store_stage(buf ^ 1, st);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds rows 4*(lane/16)+j of each 16-row tile, column lane%16 ----
+  const float ts0 = (FMT == FMT_NVFP4) ? p.w0.tscale[e] : 1.0f;
+  const float ts1 = (FMT == FMT_NVFP4) ? p.w1.tscale[e] : 1.0f;
+  const int col = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = m0 + 64 * wm + 16 * r + 4 * (lane >> 4) + j;
+      if (row >= m1) continue;
+      const int orow = row;
+      if constexpr (OP == kOpGateUp) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int n = nt * (BN / 2) + 32 * wn + 16 * c + col;
+          if (n >= N) continue;
+          const float g = acc[r][c][j] * ts0;
+          const float u = acc[r][c + 2][j] * ts1;
+          const float h = g / (1.0f + expf(-g)) * u;
+          reinterpret_cast<uint16_t*>(p.out)[(size_t)orow * N + n] = f32_to_bf16(h);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int n = n0 + 64 * wn + 16 * c + col;
+          if (n >= N) continue;
+          reinterpret_cast<float*>(p.out)[(size_t)orow * N + n] = acc[r][c][j] * ts0;
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int OP>
+hipError_t launch_t(GemmParams p, int n_row_tiles, hipStream_t s) {
+  const int ntn = (OP == kOpGateUp) ? (p.w0.rows + BN / 2 - 1) / (BN / 2) : (p.w0.rows + BN - 1) / BN;
+  p.ntn = ntn;
+  p.max_rt = n_row_tiles;
+  const int per = (n_row_tiles * ntn + kXcds - 1) / kXcds;
+  if (per == 0) return hipSuccess;
+  return launch(grouped_gemm_kernel<FMT, OP>, dim3(per * kXcds), dim3(256), 0, s, p);
+}
+
+template <int FMT>
+hipError_t launch_fmt(int op, const GemmParams& p, int n_row_tiles, hipStream_t s) {
+  return op == kOpGateUp ? launch_t<FMT, kOpGateUp>(p, n_row_tiles, s)
+                         : launch_t<FMT, kOpDown>(p, n_row_tiles, s);
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
+                               const int* tiles, const int* n_tiles, int max_tiles,
+                               const uint16_t* in, void* out, hipStream_t s) {
+  GemmParams p;
+  p.w0 = w0;
+  p.w1 = w1;
+  p.in = in;
+  p.out = out;
+  p.topk = g.topk;
+  p.T = g.T;
+  p.offsets = g.offsets;
+  p.perm_to_pair = g.perm_to_pair;
+  p.ntn = 0;
+  p.max_rt = 0;
+  p.in_rows_total = g.T * g.topk;
+  int nrt;
+  if (g.shared) {
+    p.tiles = nullptr;
+    p.n_tiles = nullptr;
+    nrt = (g.T + BM - 1) / BM;
+    p.in_rows = g.T;
+  } else {
+    p.tiles = reinterpret_cast<const int2*>(tiles);
+    p.n_tiles = n_tiles;
+    nrt = max_tiles;
+    p.in_rows = (op == kOpGateUp) ? g.T : g.T * g.topk;
+  }
+  switch (w0.fmt) {
+    case FMT_NVFP4: return launch_fmt<FMT_NVFP4>(op, p, nrt, s);
+    case FMT_MXFP4: return launch_fmt<FMT_MXFP4>(op, p, nrt, s);
+    case FMT_FP8: return launch_fmt<FMT_FP8>(op, p, nrt, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

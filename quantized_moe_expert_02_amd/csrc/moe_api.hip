@@ -114,7 +114,11 @@ struct WsPlan {
 
 constexpr int kDecodeRows = 8;
 
-constexpr int kTileM = 128;  // rows per grouped-GEMM tile
+constexpr int kTileM = kGemmTileM;  // rows per grouped-GEMM tile
+// Calls with at most this many tokens have no group larger than one GEMV
+// pass (a token picks an expert at most once) and stream each expert's
+// weights once; larger calls run the tiled grouped GEMM.
+constexpr int kGemvMaxRows = 16;
 
 WsPlan plan(const moe_layer_desc* L, int T) {
   WsPlan p;
@@ -201,13 +205,17 @@ int32_t run_route(const moe_layer_desc* L, const uint16_t* x, float* logits, int
   return hip_status(launch_topk(a, s));
 }
 
+// tiles_ready: the tile list in ws was written by launch_permute for these
+// offsets (moe_layer_forward); otherwise it is rebuilt here when needed.
 int32_t run_experts(int op, const moe_layer_desc* L, int shared, const int* offsets,
                     const int* perm_to_pair, const int* active, int T, const uint16_t* in,
-                    void* out, void* ws, const WsPlan& p, hipStream_t s) {
+                    void* out, void* ws, const WsPlan& p, bool tiles_ready, hipStream_t s) {
   GroupArgs g;
   g.offsets = offsets;
   g.perm_to_pair = perm_to_pair;
-  const bool groups_ready = shared || active != nullptr;
+  const bool gemm = T > kGemvMaxRows;
+  const bool groups_ready = shared || (gemm ? tiles_ready : active != nullptr);
+  if (gemm && !shared) active = at<int>(ws, p.nact);
   if (active == nullptr && !shared) active = at<int>(ws, p.nact);
   g.act = active ? active + 1 : nullptr;
   g.n_act = active;
@@ -230,6 +238,9 @@ int32_t run_experts(int op, const moe_layer_desc* L, int shared, const int* offs
     w0 = wdesc(shared ? L->sh_down : L->down);
     w1 = w0;
   }
+  if (gemm)
+    return hip_status(launch_grouped_gemm(op, w0, w1, g, at<int>(ws, p.tiles),
+                                          at<int>(ws, p.ntiles), p.max_tiles, in, out, s));
   return hip_status(launch_expert_gemv(op, w0, w1, g, in, out, s));
 }
 
@@ -316,7 +327,7 @@ int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
   if (!shared && (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)))
     return MOE_ERR_WORKSPACE;
   return run_experts(op, L, shared, offsets, perm_to_pair, shared ? nullptr : active_experts, T,
-                     in, out, ws, p, static_cast<hipStream_t>(stream));
+                     in, out, ws, p, false, static_cast<hipStream_t>(stream));
 }
 
 int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pair_to_perm,
@@ -395,17 +406,20 @@ int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T,
   uint16_t* h = at<uint16_t>(ws, p.h);
   float* y = at<float>(ws, p.y);
   const int* active = at<int>(ws, p.nact);
-  if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, x, h, ws, p, s)))
+  if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, x, h, ws, p, true,
+                        s)))
     return st;
-  if ((st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, h, y, ws, p, s))) return st;
+  if ((st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, h, y, ws, p, true, s)))
+    return st;
   float* ys = nullptr;
   if (L->has_shared) {
     uint16_t* hs = at<uint16_t>(ws, p.hs);
     ys = at<float>(ws, p.ys);
     if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T, x, hs, ws, p,
-                          s)))
+                          true, s)))
       return st;
-    if ((st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hs, ys, ws, p, s)))
+    if ((st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hs, ys, ws, p, true,
+                          s)))
       return st;
   }
   return hip_status(launch_combine(y, w, pair2p, ys, T, L->top_k, L->H, out, s));

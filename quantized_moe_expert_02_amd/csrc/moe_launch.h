@@ -76,6 +76,13 @@ struct GroupArgs {
 };
 hipError_t launch_expert_gemv(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
                               const uint16_t* in, void* out, hipStream_t s);
+// Tiled grouped GEMM (row groups of any size) over the tile list of
+// launch_permute / launch_groups_from_offsets: tiles int2 (expert, first
+// permuted row) of kGemmTileM rows.  Shared expert (g.shared): tiles unused.
+constexpr int kGemmTileM = 128;
+hipError_t launch_grouped_gemm(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
+                               const int* tiles, const int* n_tiles, int max_tiles,
+                               const uint16_t* in, void* out, hipStream_t s);
 
 // ---- fused decode lowering (T <= 8) -----------------------------------------
 struct DecodePlan {

@@ -30,6 +30,23 @@ SMALL = {
                                top_k=2, fmt=synth.FMT_FP8, I_shared=272, shared_fmt=synth.FMT_FP8),
     "nvfp4_t3_k1": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t3_k1", T=3, H=256, E=4, I=128,
                                 top_k=1),
+    # above the fused decode size, at most one GEMV pass per group
+    "nvfp4_t12": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t12", T=12, H=288, E=8, I=96,
+                              top_k=3, I_shared=64, shared_fmt=synth.FMT_MXFP4),
+}
+
+
+# Layers with T > 16 (tiled grouped GEMM): expert groups span several
+# 128-row tiles, with ragged row tails, column tails (I, H not multiples of
+# the 64/128-wide column tiles) and K tails (H, I not multiples of 64).
+MID = {
+    "nvfp4_mid": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_mid", T=300, H=352, E=6, I=160,
+                              top_k=3, I_shared=96, shared_fmt=synth.FMT_FP8),
+    "mxfp4_mid": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp4_mid", T=200, H=416, E=5, I=224,
+                              top_k=2, fmt=synth.FMT_MXFP4, I_shared=64,
+                              shared_fmt=synth.FMT_NVFP4, zipf_s=1.1),
+    "fp8_mid": synth.scaled(W["tiny_nvfp4_t4"], name="fp8_mid", T=260, H=336, E=4, I=144,
+                            top_k=2, fmt=synth.FMT_FP8, I_shared=272, shared_fmt=synth.FMT_FP8),
 }
 
 
@@ -58,8 +75,66 @@ def test_layer_decode_fp8_wide_sampled():
     say(f"[gpu] fp8 wide: rel={r['rel']:.2e} worst={r['worst']:.2e}")
 
 
-def test_layer_is_deterministic():
-    w = SMALL["nvfp4_ragged"]
+@pytest.mark.parametrize("name", list(MID))
+def test_layer_grouped_gemm(name):
+    w = MID[name]
+    say(f"[gpu] layer {name}: T={w.T} H={w.H} E={w.E} I={w.I} k={w.top_k} fmt={w.fmt}")
+    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), what=name)
+    counts = np.bincount(r["ids"].reshape(-1), minlength=w.E)
+    say(f"[gpu] layer {name}: rel={r['rel']:.2e} worst={r['worst']:.2e} groups={counts.tolist()}")
+    assert counts.max() > 128                # at least one group spans two row tiles
+
+
+# Group sizes around the 128-row tile: empty, 1, one short of a tile, exactly
+# one, one over, exactly two, and a ragged multi-tile group.
+EDGE_COUNTS = [0, 1, 127, 128, 129, 0, 256, 300]
+
+
+@pytest.mark.parametrize("fmt,H,I", [(synth.FMT_NVFP4, 352, 160), (synth.FMT_MXFP4, 416, 224),
+                                     (synth.FMT_FP8, 336, 144)])
+def test_grouped_gemm_tile_edges(fmt, H, I):
+    """moe_expert_gemm on a hand-made grouping (k = 1, tokens shuffled)."""
+    E = len(EDGE_COUNTS)
+    T = sum(EDGE_COUNTS)
+    w = synth.scaled(W["tiny_nvfp4_t4"], name=f"edges_{fmt}", T=T, H=H, E=E, I=I, top_k=1, fmt=fmt)
+    say(f"[gpu] grouped GEMM tile edges fmt={fmt} T={T} H={H} I={I} counts={EDGE_COUNTS}")
+    L = layer_for(w)
+    rng = np.random.default_rng(5)
+    ids = rng.permutation(np.repeat(np.arange(E), EDGE_COUNTS)).astype(np.int32).reshape(T, 1)
+    G = O.permute(ids, E)
+    assert np.array_equal(G.counts, EDGE_COUNTS)
+    x_bits = synth.make_x(w)
+    x64 = O.bf16_value(x_bits)
+    dl = device_layer(L)
+    ws = dl.workspace(T)
+    offs = torch.from_numpy(G.offsets).cuda()
+    p2 = torch.from_numpy(G.perm_to_pair).cuda()
+    h = torch.empty((T, I), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, dl.desc, 0, offs, p2, None, T,
+                        bf16_tensor(x_bits), h, ws)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    moe.moe_expert_gemm(moe.MOE_OP_DOWN, dl.desc, 0, offs, p2, None, T, h, y, ws)
+    torch.cuda.synchronize()
+    got_h = O.bf16_value(bf16_bits(h))
+    got_y = y.cpu().numpy()
+    ref_h = np.zeros((T, I))
+    ref_y = np.zeros((T, H))
+    for e in range(E):
+        rows = np.arange(G.offsets[e], G.offsets[e + 1])
+        if rows.size == 0:
+            continue
+        toks = G.perm_to_pair[rows]        # k = 1: pair index = token
+        ref_h[rows] = O.ffn_gate_up(x64[toks], F.dequant(L.gate, e), F.dequant(L.up, e))
+        # down from the GPU's own h, so one bf16 rounding step of h does not
+        # propagate into y
+        ref_y[rows] = O.ffn_down(got_h[rows], F.dequant(L.down, e))
+    assert_close(got_h, ref_h, f"edges {fmt} h")
+    assert_close(got_y, ref_y, f"edges {fmt} y")
+
+
+@pytest.mark.parametrize("name", ["nvfp4_ragged", "fp8_mid"])
+def test_layer_is_deterministic(name):
+    w = SMALL.get(name) or MID[name]
     dl = device_layer(layer_for(w))
     from gpu_util import run_layer
     x = synth.make_x(w)
