@@ -108,6 +108,9 @@ struct WsPlan {
   int P, NB, max_tiles;
   size_t part, amax, ids, w, counts, offsets, p2pair, pair2p, hist, act, nact, tiles, ntiles, h,
       hs, y, ys, total;
+  // matrix-core router (T > kGemvMaxRows): split router planes and w^2 sums
+  bool mfma_router;
+  size_t planes, wsq;
   // fused decode (T <= kDecodeRows): router slice sums
   size_t dpart, dapart;
 };
@@ -119,6 +122,8 @@ constexpr int kTileM = kGemmTileM;  // rows per grouped-GEMM tile
 // pass (a token picks an expert at most once) and stream each expert's
 // weights once; larger calls run the tiled grouped GEMM.
 constexpr int kGemvMaxRows = 16;
+// The matrix-core router's error bound assumes H * 2^-23 << 1.
+constexpr int kMfmaRouterMaxH = 1 << 16;
 
 WsPlan plan(const moe_layer_desc* L, int T) {
   WsPlan p;
@@ -134,8 +139,11 @@ WsPlan plan(const moe_layer_desc* L, int T) {
     return at;
   };
   p.dp = decode_plan(T, L->H, E);
+  p.mfma_router = T > kGemvMaxRows && L->H <= kMfmaRouterMaxH;
+  const size_t amax_n = p.mfma_router ? (size_t)router_mfma_cols(E) * T
+                                      : (size_t)p.rp.RS * p.rp.CS * T;
   p.part = take((size_t)p.rp.RS * T * E * 4);
-  p.amax = take((size_t)p.rp.RS * p.rp.CS * T * 4);
+  p.amax = take(amax_n * 4);
   p.ids = take((size_t)p.P * 4);
   p.w = take((size_t)p.P * 4);
   p.counts = take((size_t)E * 4);
@@ -151,6 +159,11 @@ WsPlan plan(const moe_layer_desc* L, int T) {
   p.hs = take(L->has_shared ? (size_t)T * L->I_shared * 2 : 0);
   p.y = take((size_t)p.P * L->H * 4);
   p.ys = take(L->has_shared ? (size_t)T * L->H * 4 : 0);
+  p.planes = p.wsq = 0;
+  if (p.mfma_router) {
+    p.planes = take((size_t)3 * E * L->H * 2);
+    p.wsq = take(router_mfma_wsq_count(L->H, E) * 8);
+  }
   p.dpart = p.dapart = 0;
   if (T <= kDecodeRows) {
     p.dpart = take((size_t)p.dp.RS * T * E * 4);
@@ -189,14 +202,27 @@ int32_t run_route(const moe_layer_desc* L, const uint16_t* x, float* logits, int
     a.part = logits;
     a.RS = 1;
   } else {
-    hipError_t e = launch_router_logits(x, L->router_w, T, L->H, L->E, p.rp, at<float>(ws, p.part),
-                                        at<float>(ws, p.amax), s);
-    if (e != hipSuccess) return hip_status(e);
     a.mode = 1;
     a.part = at<float>(ws, p.part);
-    a.RS = p.rp.RS;
     a.amax = at<float>(ws, p.amax);
-    a.CS = p.rp.CS;
+    if (p.mfma_router) {
+      hipError_t e = launch_router_mfma(x, L->router_w, T, L->H, L->E, at<uint16_t>(ws, p.planes),
+                                        at<double>(ws, p.wsq), at<float>(ws, p.part),
+                                        at<float>(ws, p.amax), s);
+      if (e != hipSuccess) return hip_status(e);
+      a.RS = 1;
+      a.CS = router_mfma_cols(L->E);
+      a.bound_scale = router_mfma_bound_scale(L->H);
+    } else {
+      // float64 slice sums rounded once to fp32: error <= 2^-23 * sum|x||w|
+      hipError_t e = launch_router_logits(x, L->router_w, T, L->H, L->E, p.rp,
+                                          at<float>(ws, p.part), at<float>(ws, p.amax), s);
+      if (e != hipSuccess) return hip_status(e);
+      a.RS = p.rp.RS;
+      a.CS = p.rp.CS;
+      a.bound_scale = 0x1p-22;
+    }
+    a.bound_abs = 0.0;
     a.bias = L->router_bias;
     a.x = x;
     a.wr = L->router_w;

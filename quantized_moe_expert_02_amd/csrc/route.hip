@@ -12,7 +12,9 @@
 // its error is below 2^-23 * sum_h |x_h||w_he| (+|b_e|).  The top-k kernel
 // accepts the fast order when every adjacent gap among the top k+1 exceeds
 // twice that bound; otherwise it recomputes the contested logits with a
-// compensated (double-float64) sum and decides on those.
+// compensated (double-float64) sum and decides on those.  Large batches
+// compute the fast logits on the matrix cores instead (router_gemm.hip),
+// with a bound of their own; the top-k below serves both.
 #include "moe_launch.h"
 #include "topk_core.cuh"
 
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
       if (a.logits_out != nullptr) a.logits_out[(size_t)t * E + e] = static_cast<float>(l);
     }
   }
-  // Error bound of the fast logits (mode 1): 2^-23 * max_e sum|x||w| (+|b|).
+  // Error bound of the fast logits (mode 1): the router kernel's per-block
+  // factors (amax) times its scale; see TopkArgs.
   float m = 0.f;
   if (a.mode == 1) {
     for (int i = threadIdx.x; i < a.RS * a.CS; i += blockDim.x) {
@@ -132,13 +135,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   __syncthreads();
   float am = 0.f;
   for (int i = 0; i < (int)(blockDim.x / kWave); ++i) am = fmaxf(am, amax_w[i]);
-  // With one slice (RS == 1) the max over column blocks is the max over
-  // experts; the bias term is added on top as a safe over-estimate.
+  // The max over column blocks (and slices) bounds every expert of the
+  // token; |bias| joins the maximum as a safe over-estimate of the float64
+  // bias addition.
   BlockTopkArgs ta;
   ta.E = E;
   ta.k = a.k;
   ta.renorm = a.renorm;
-  ta.bound = (a.mode == 1) ? static_cast<double>(am) * 2.0 * 0x1p-23 : 0.0;
+  ta.bound = (a.mode == 1) ? static_cast<double>(am) * a.bound_scale + a.bound_abs : 0.0;
   ta.certify = a.mode == 1;
   ta.xrow = a.x ? a.x + (size_t)t * a.H : nullptr;
   ta.wr = a.wr;

@@ -54,7 +54,10 @@ __device__ inline double dd_logit(const uint16_t* __restrict__ xrow, const float
     two_sum(s, static_cast<double>(bias[e]), s, err);
     c += err;
   }
-  return s + c;
+  // An infinite or NaN term makes the running sum s the IEEE result of the
+  // exact sum (finite bf16 x fp32 terms cannot overflow float64), while the
+  // compensation has turned NaN: return s alone then.
+  return (s - s == 0.0) ? s + c : s;
 }
 
 struct TopkToken {
@@ -292,7 +295,9 @@ __device__ inline void block_topk(BlockTopkSmem& sm, const BlockTopkArgs& a) {
     }
     const int any_bad = __syncthreads_or(bad);
     if (any_bad) {
-      const int all = __syncthreads_or(bad == 2);
+      // A non-finite bound (possible overflow in the fast sum) says nothing
+      // about any logit: recompute all of them.
+      const int all = __syncthreads_or(bad == 2) || !(a.bound < __builtin_inf());
       // Every exact top-k member has a fast logit >= (k-th fast value) - 2*bound.
       const double thr = sm.topv[k - 1] - 2.0 * a.bound;
       if (threadIdx.x == 0) sm.ncand = 0;

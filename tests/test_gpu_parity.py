@@ -165,6 +165,74 @@ def test_route_topk_given_logits_exact():
     assert_close(wt.cpu().numpy()[ok], ref_w[ok], "given-logit weights")
 
 
+def _tie_router(H, E, seed=3):
+    """Router weights with exact ties (duplicated columns) and 1-ulp near
+    ties, biased so that the tied experts sit at the top-k boundary."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((H, E)) * 0.05).astype(np.float32)
+    w[:, 10] = w[:, 3]                          # exact tie with expert 3
+    w[:, 20] = w[:, 3]
+    w[7, 20] = np.nextafter(w[7, 3], np.float32(1))   # near tie
+    w[:, 33] = w[:, 12]
+    b = np.zeros(E, dtype=np.float32)
+    b[[3, 10, 20, 12, 33]] = [2.0, 2.0, 2.0, 1.5, 1.5]
+    return w, b
+
+
+def _special_rows(x_bits):
+    x = x_bits.copy()
+    x[1, 5] = 0x7F80            # +inf
+    x[2, 9] = 0x7FC0            # NaN
+    x[3, :] = 0                 # all zero: logits = bias, exact ties
+    x[4, :] = 0x7F7F            # bf16 max: fp32 sums overflow
+    x[5, 17] = 0xFF80           # -inf
+    return x
+
+
+@pytest.mark.parametrize("T", [12, 40])
+def test_route_certified_ties_and_specials(T):
+    """moe_route_topk from activations (float64 router for T <= 16, matrix-core
+    router above) on ties, near ties and non-finite / overflowing rows."""
+    H, E, k = 352, 64, 6
+    w_ = synth.scaled(W["tiny_nvfp4_t4"], name="route_ties", T=T, H=H, E=E, top_k=k)
+    import dataclasses
+    wr, b = _tie_router(H, E)
+    L = dataclasses.replace(layer_for(w_), router_w=wr, router_bias=b)
+    x_bits = _special_rows(synth.make_x(w_))
+    say(f"[gpu] route ties/specials T={T}")
+    dl = device_layer(L)
+    x = bf16_tensor(x_bits)
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route_topk(dl.desc, x, lg, T, ids, wt, dl.workspace(T))
+    torch.cuda.synchronize()
+    ref = O.route(x_bits, wr, b, k, True)
+    got = ids.cpu().numpy()
+    bad = np.nonzero(np.any(got != ref.ids, axis=1))[0]
+    assert bad.size == 0, f"tokens {bad}: got {got[bad[:3]]} want {ref.ids[bad[:3]]}"
+    assert_close(wt.cpu().numpy(), ref.weights, "tie routing weights")
+    say(f"[gpu] route ties T={T}: oracle recomputed {int(ref.recomputed.sum())} of {T} tokens")
+
+
+def test_decode_route_ties_and_specials():
+    """The fused decode path (T = 8) on the same rows: expert ids exact."""
+    H, E, k, T = 352, 64, 6, 8
+    w_ = synth.scaled(W["tiny_nvfp4_t4"], name="route_ties", T=T, H=H, E=E, top_k=k)
+    import dataclasses
+    wr, b = _tie_router(H, E)
+    L = dataclasses.replace(layer_for(w_), router_w=wr, router_bias=b)
+    x_bits = _special_rows(synth.make_x(w_))
+    say("[gpu] decode route ties/specials T=8")
+    dl = device_layer(L)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    moe.moe_layer_forward(dl.desc, bf16_tensor(x_bits), T, out, dl.workspace(T), dbg_ids=ids)
+    torch.cuda.synchronize()
+    ref = O.route(x_bits, wr, b, k, True)
+    assert np.array_equal(ids.cpu().numpy(), ref.ids)
+
+
 @pytest.mark.parametrize("T,k,E,skew", [(1, 10, 512, 0), (8, 10, 512, 1), (300, 7, 96, 1),
                                         (8192, 10, 512, 1), (1500, 1, 3, 0)])
 def test_permute_bit_exact(T, k, E, skew):
