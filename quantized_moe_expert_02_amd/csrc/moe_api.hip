@@ -110,7 +110,7 @@ struct WsPlan {
       hs, y, ys, total;
   // matrix-core router (T > kGemvMaxRows): split router planes and w^2 sums
   bool mfma_router;
-  size_t planes, wsq;
+  size_t planes, wrt, wsq;
   // fused decode (T <= kDecodeRows): router slice sums
   size_t dpart, dapart;
 };
@@ -159,9 +159,10 @@ WsPlan plan(const moe_layer_desc* L, int T) {
   p.hs = take(L->has_shared ? (size_t)T * L->I_shared * 2 : 0);
   p.y = take((size_t)p.P * L->H * 4);
   p.ys = take(L->has_shared ? (size_t)T * L->H * 4 : 0);
-  p.planes = p.wsq = 0;
+  p.planes = p.wrt = p.wsq = 0;
   if (p.mfma_router) {
     p.planes = take((size_t)3 * E * L->H * 2);
+    p.wrt = take((size_t)E * L->H * 4);
     p.wsq = take(router_mfma_wsq_count(L->H, E) * 8);
   }
   p.dpart = p.dapart = 0;
@@ -201,15 +202,18 @@ int32_t run_route(const moe_layer_desc* L, const uint16_t* x, float* logits, int
     a.mode = 0;
     a.part = logits;
     a.RS = 1;
+    a.wave = T > kGemvMaxRows;
   } else {
     a.mode = 1;
     a.part = at<float>(ws, p.part);
     a.amax = at<float>(ws, p.amax);
     if (p.mfma_router) {
       hipError_t e = launch_router_mfma(x, L->router_w, T, L->H, L->E, at<uint16_t>(ws, p.planes),
-                                        at<double>(ws, p.wsq), at<float>(ws, p.part),
-                                        at<float>(ws, p.amax), s);
+                                        at<float>(ws, p.wrt), at<double>(ws, p.wsq),
+                                        at<float>(ws, p.part), at<float>(ws, p.amax), s);
       if (e != hipSuccess) return hip_status(e);
+      a.wave = 1;
+      a.wrt = at<float>(ws, p.wrt);
       a.RS = 1;
       a.CS = router_mfma_cols(L->E);
       a.bound_scale = router_mfma_bound_scale(L->H);

@@ -41,6 +41,10 @@ struct TopkArgs {
   int* recomputed;    // [T] or nullptr
   // mode 1: per-logit error bound = bound_scale * max(amax over blocks, |bias|) + bound_abs
   double bound_scale, bound_abs;
+  // One wavefront per token (large T) instead of one block; in mode 1 this
+  // needs wrt, the router weights transposed to [E][H], for the recompute.
+  int wave;
+  const float* wrt;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
@@ -48,13 +52,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // planes, fp32 step sums added in float64.  Writes logits [T][E] (no bias)
 // and amax [router_mfma_cols(E)][T]; the top-k bound is
 // router_mfma_bound_scale(H) times the maximum of amax over blocks.
-// planes: [3][E][H] bf16 scratch; wsq: router_mfma_wsq_count(H, E) doubles.
+// planes: [3][E][H] bf16 scratch; wrt: [E][H] fp32 (Wr transposed, written
+// for the top-k recompute); wsq: router_mfma_wsq_count(H, E) doubles.
 int router_mfma_cols(int E);
 size_t router_mfma_wsq_count(int H, int E);
 double router_mfma_bound_scale(int H);
 hipError_t launch_router_mfma(const uint16_t* x, const float* wr, int T, int H, int E,
-                              uint16_t* planes, double* wsq, float* logits, float* amax,
-                              hipStream_t s);
+                              uint16_t* planes, float* wrt, double* wsq, float* logits,
+                              float* amax, hipStream_t s);
 
 // ---- grouping -------------------------------------------------------------
 constexpr int kPermChunk = 1024;

@@ -153,6 +153,55 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   block_topk(sm, ta);
 }
 
+// Large batches: one wavefront per token, kWaveTopkTokens tokens per block.
+// Only wave-level synchronisation is used, so a wave past the last token can
+// leave early.
+constexpr int kWaveTopkTokens = 4;
+
+__global__ __launch_bounds__(kWave * kWaveTopkTokens) void topk_wave_kernel(TopkArgs a) {
+  __shared__ double vals[kWaveTopkTokens][kMaxExperts];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kWaveTopkTokens + wave;
+  if (t >= a.T) return;
+  const int E = a.E;
+  double* v = vals[wave];
+  float m = 0.f;
+  if (a.mode == 0) {
+    for (int e = lane; e < E; e += kWave) v[e] = static_cast<double>(a.part[(size_t)t * E + e]);
+  } else {
+    for (int e = lane; e < E; e += kWave) {
+      double l = static_cast<double>(a.part[(size_t)t * E + e]);  // one slice
+      if (a.bias != nullptr) {
+        l += static_cast<double>(a.bias[e]);
+        m = fmaxf(m, fabsf(a.bias[e]));
+      }
+      v[e] = l;
+      if (a.logits_out != nullptr) a.logits_out[(size_t)t * E + e] = static_cast<float>(l);
+    }
+    for (int c = lane; c < a.CS; c += kWave) m = fmaxf(m, a.amax[(size_t)c * a.T + t]);
+  }
+  m = wave_max_f(m);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  TopkToken tk;
+  tk.vals = v;
+  tk.E = E;
+  tk.k = a.k;
+  tk.renorm = a.renorm;
+  tk.bound = (a.mode == 1) ? static_cast<double>(m) * a.bound_scale + a.bound_abs : 0.0;
+  tk.certify = a.mode == 1;
+  tk.xrow = a.x ? a.x + (size_t)t * a.H : nullptr;
+  tk.wr = a.wrt;
+  tk.wr_sh = 1;
+  tk.wr_se = (size_t)a.H;
+  tk.bias = a.bias;
+  tk.H = a.H;
+  tk.ids = a.ids + (size_t)t * a.k;
+  tk.w = a.w + (size_t)t * a.k;
+  tk.recomputed = a.recomputed ? a.recomputed + t : nullptr;
+  wave_topk(tk);
+}
+
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E,
@@ -162,6 +211,11 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.wave) {
+    if (a.mode == 1 && (a.RS != 1 || a.wrt == nullptr)) return hipErrorInvalidValue;
+    return launch(topk_wave_kernel, dim3((a.T + kWaveTopkTokens - 1) / kWaveTopkTokens),
+                  dim3(kWave * kWaveTopkTokens), 0, s, a);
+  }
   return launch(topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
 }
 

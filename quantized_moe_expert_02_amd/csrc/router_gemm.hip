@@ -49,10 +49,13 @@ __device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uin
   lo = static_cast<uint16_t>(__float_as_uint(r1) >> 16);   // exact unless |w| < 2^-110
 }
 
-// Wr [H][E] fp32 -> planes [3][E][H] bf16 and wsq [HB][E] float64 sums of w^2
-// over router rows [hb*128, +128).  Block: 64 experts x 128 rows; lane = expert.
+// Wr [H][E] fp32 -> planes [3][E][H] bf16, a transposed fp32 copy wrt [E][H]
+// (for the exact recompute of contested logits, read along h), and wsq
+// [HB][E] float64 sums of w^2 over router rows [hb*128, +128).
+// Block: 64 experts x 128 rows; lane = expert.
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, int H,
                                                            int E, uint16_t* __restrict__ planes,
+                                                           float* __restrict__ wrt,
                                                            double* __restrict__ wsq) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + lane;
@@ -64,10 +67,13 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
       const int h = h0 + c;
       if (h >= H) break;  // H % 8 == 0: a group of 8 rows is all in or all out
       uint32_t p[3][4];
+      float wv[8];
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
         const float w0 = wr[(size_t)(h + i) * E + e];
         const float w1 = wr[(size_t)(h + i + 1) * E + e];
+        wv[i] = w0;
+        wv[i + 1] = w1;
         sq = fma(static_cast<double>(w0), static_cast<double>(w0), sq);
         sq = fma(static_cast<double>(w1), static_cast<double>(w1), sq);
         uint16_t a0, a1, a2, c0, c1, c2;
@@ -81,6 +87,9 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
       for (int s = 0; s < 3; ++s)
         *reinterpret_cast<u32x4*>(planes + ((size_t)s * E + e) * H + h) =
             u32x4{p[s][0], p[s][1], p[s][2], p[s][3]};
+      float* wt = wrt + (size_t)e * H + h;
+      *reinterpret_cast<f32x4*>(wt) = f32x4{wv[0], wv[1], wv[2], wv[3]};
+      *reinterpret_cast<f32x4*>(wt + 4) = f32x4{wv[4], wv[5], wv[6], wv[7]};
     }
   }
   __shared__ double red[4][64];
@@ -270,11 +279,11 @@ double router_mfma_bound_scale(int H) {
 }
 
 hipError_t launch_router_mfma(const uint16_t* x, const float* wr, int T, int H, int E,
-                              uint16_t* planes, double* wsq, float* logits, float* amax,
-                              hipStream_t s) {
+                              uint16_t* planes, float* wrt, double* wsq, float* logits,
+                              float* amax, hipStream_t s) {
   const int HB = (H + kSplitRows - 1) / kSplitRows;
   hipError_t err = launch(router_split_kernel, dim3((E + 63) / 64, HB), dim3(256), 0, s, wr, H, E,
-                          planes, wsq);
+                          planes, wrt, wsq);
   if (err != hipSuccess) return err;
   RouterMfmaArgs a;
   a.x = x;

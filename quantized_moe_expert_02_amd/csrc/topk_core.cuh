@@ -29,17 +29,58 @@ __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e
 }
 
 // Compensated float64 logit of expert e for one token (whole wave; every lane
-// returns the same value).
-__device__ inline double dd_logit(const uint16_t* __restrict__ xrow, const float* __restrict__ wr,
-                                  int H, int E, int e, const float* bias) {
+// returns the same value).  Router weight (h, e) is w[h*sh + e*se]: sh = E,
+// se = 1 for the [H][E] layout, sh = 1, se = H for a transposed [E][H] copy.
+// Each lane takes 8 consecutive h per step, and the loads of up to 4 steps
+// are issued before any of them is summed, so one call waits about one
+// memory round trip rather than one per step.  Needs H % 8 == 0 and, for
+// sh == 1, 16-byte aligned rows of w.
+__device__ __forceinline__ void dd_add(double& s, double& c, double p) {
+  double err;
+  two_sum(s, p, s, err);
+  c += err;
+}
+
+__device__ inline double dd_logit(const uint16_t* __restrict__ xrow, const float* __restrict__ w,
+                                  size_t sh, size_t se, int H, int e, const float* bias) {
+  constexpr int D = 4;
   const int lane = __lane_id();
   double s = 0.0, c = 0.0;
-  for (int h = lane; h < H; h += kWave) {
-    const double p = static_cast<double>(bf16_to_f32(xrow[h])) *
-                     static_cast<double>(wr[(size_t)h * E + e]);
-    double err;
-    two_sum(s, p, s, err);
-    c += err;
+  const float* we = w + (size_t)e * se;
+  for (int hb = 0; hb < H; hb += 8 * kWave * D) {
+    u32x4 xv[D];
+    f32x4 w0[D], w1[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int h = hb + 8 * (lane + kWave * d);
+      const bool on = h < H;
+      const int hh = on ? h : 0;
+      xv[d] = *reinterpret_cast<const u32x4*>(xrow + hh);
+      if (sh == 1) {
+        w0[d] = *reinterpret_cast<const f32x4*>(we + hh);
+        w1[d] = *reinterpret_cast<const f32x4*>(we + hh + 4);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w0[d][j] = we[(size_t)(hh + j) * sh];
+          w1[d][j] = we[(size_t)(hh + 4 + j) * sh];
+        }
+      }
+      if (!on) xv[d] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (hb + 8 * (lane + kWave * d) >= H) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float xl = __uint_as_float(xv[d][j] << 16);
+        const float xh = __uint_as_float(xv[d][j] & 0xffff0000u);
+        const float wl = (j < 2) ? w0[d][2 * j] : w1[d][2 * j - 4];
+        const float wh = (j < 2) ? w0[d][2 * j + 1] : w1[d][2 * j - 3];
+        dd_add(s, c, static_cast<double>(xl) * static_cast<double>(wl));
+        dd_add(s, c, static_cast<double>(xh) * static_cast<double>(wh));
+      }
+    }
   }
   // Pairwise combine: both lanes of a pair compute identical values.
   for (int m = 1; m < kWave; m <<= 1) {
@@ -49,11 +90,7 @@ __device__ inline double dd_logit(const uint16_t* __restrict__ xrow, const float
     two_sum(s, os, s, err);
     c = (c + oc) + err;
   }
-  if (bias != nullptr) {
-    double err;
-    two_sum(s, static_cast<double>(bias[e]), s, err);
-    c += err;
-  }
+  if (bias != nullptr) dd_add(s, c, static_cast<double>(bias[e]));
   // An infinite or NaN term makes the running sum s the IEEE result of the
   // exact sum (finite bf16 x fp32 terms cannot overflow float64), while the
   // compensation has turned NaN: return s alone then.
@@ -66,7 +103,8 @@ struct TopkToken {
   double bound;        // error bound of vals (ignored when !certify)
   bool certify;
   const uint16_t* xrow;  // for the recompute (certify only)
-  const float* wr;
+  const float* wr;       // router weights, element (h, e) at wr[h*wr_sh + e*wr_se]
+  size_t wr_sh, wr_se;
   const float* bias;
   int H;
   int* ids;            // [k] out
@@ -135,18 +173,21 @@ __device__ inline void wave_topk(const TopkToken& a) {
     if (a.recomputed != nullptr && lane == 0) *a.recomputed = ok ? 0 : 1;
     if (!ok) {
       // Every exact top-k member has a fast logit >= (k-th fast value) - 2*bound.
+      // A non-finite value among the top k+1 or a non-finite bound says
+      // nothing about the others: then every logit is recomputed.
+      const bool all = !finite || !(a.bound < __builtin_inf());
       const double thr = __shfl(top_v, k - 1, kWave) - 2.0 * a.bound;
       const int nper = (E + kWave - 1) / kWave;
       for (int i = 0; i < nper; ++i) {
         const int e = lane + kWave * i;
         const double v = (e < E) ? a.vals[e] : 0.0;
-        const bool cand = (e < E) && (!finite || (v == v && v >= thr));
+        const bool cand = (e < E) && (all || (v == v && v >= thr));
         if (e < E && !cand) excl |= 1u << i;
         uint64_t mask = __ballot(cand);
         while (mask) {
           const int l = __builtin_ctzll(mask);
           mask &= mask - 1;
-          const double val = dd_logit(a.xrow, a.wr, a.H, E, l + kWave * i, a.bias);
+          const double val = dd_logit(a.xrow, a.wr, a.wr_sh, a.wr_se, a.H, l + kWave * i, a.bias);
           if (lane == 0) a.vals[l + kWave * i] = val;
         }
       }
@@ -311,7 +352,7 @@ __device__ inline void block_topk(BlockTopkSmem& sm, const BlockTopkArgs& a) {
       __syncthreads();
       for (int i = wave; i < sm.ncand; i += nwaves) {
         const int c = sm.cand[i];
-        const double val = dd_logit(a.xrow, a.wr, a.H, E, c, a.bias);
+        const double val = dd_logit(a.xrow, a.wr, (size_t)E, 1, a.H, c, a.bias);
         if (lane == 0) sm.v[c] = val;
       }
       __syncthreads();
