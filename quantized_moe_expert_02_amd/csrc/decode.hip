@@ -5,24 +5,24 @@
 // the weights at the memory's line rate).  On gfx950 a dependent kernel in the
 // same stream starts about 1.5 us after its predecessor ends, while a
 // cross-workgroup hand-off inside a kernel needs an agent-scope release
-// (an L2 write-back) and costs far more; so the layer runs as five short
+// (an L2 write-back) and costs far more; so the layer runs as four short
 // launches with no intra-kernel hand-off:
 //
-//   1. router partial sums over (128-row slice x 32 experts) blocks; extra
-//      blocks compute the shared expert's gate/up + SwiGLU (it does not
+//   1. router partial sums over (128-row slice x 32 experts) blocks; the
+//      first blocks compute the shared expert's gate/up + SwiGLU (it does not
 //      depend on routing);
-//   2. one block per token: sum the slices, select the top-k by rank counting,
-//      certify it against the exact logits (recomputing near ties), weights;
+//   2. one block per token: sum the slices, select the top-k (coarse
+//      threshold, then exact ranking of the candidates), certify it against
+//      the exact logits (recomputing near ties), weights;
 //   3. each active routed expert's gate/up + SwiGLU, its weights streamed once
 //      for all of its tokens (blocks are laid out per routed pair slot; the
 //      block of an expert's first pair derives the expert's (token, slot)
-//      pairs from the <= 256 routed ids, the others exit); extra blocks run
-//      the shared expert's down projection;
-//   4. each active expert's down projection;
-//   5. combine: per-expert partials in fp32, in slot order, then the shared
-//      expert, rounded once to bf16.
+//      pairs from the <= 256 routed ids, the others exit);
+//   4. per (token, 16 output columns): the down projections of the token's k
+//      slots and of the shared expert, combined in slot order in fp32 and
+//      rounded once to bf16.
 //
-// Rows of h and y are indexed by pair (t*k + j), so no permutation is needed.
+// Rows of h are indexed by pair (t*k + j), so no permutation is needed.
 #include "gemv_core.cuh"
 #include "topk_core.cuh"
 
@@ -46,17 +46,20 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
     RouterSmem r;
     GemvSmem<GemvShape<kOpGateUp>::WN, GemvShape<kOpGateUp>::WK, 2> g;
   } sm;
-  const int nrb = a.RS * a.CS;
-  if ((int)blockIdx.x >= nrb) {  // shared expert gate/up + SwiGLU
+  // The shared expert's blocks come first: they do the most work, so they
+  // should be dispatched first.
+  const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
+  if ((int)blockIdx.x < nsg) {  // shared expert gate/up + SwiGLU
     if constexpr (SFMT != 0) {
       GemvIO io{a.x, a.hs, nullptr, a.k, kInShared, a.T};
       gemv_tile<SFMT, kOpGateUp, 1, 4>(a.sg, a.su, io, GemvRows{0, 0, a.T, nullptr, nullptr},
-                                       blockIdx.x - nrb, sm.g);
+                                       blockIdx.x, sm.g);
     }
     return;
   }
+  const int rb = blockIdx.x - nsg;
   const int T = a.T, H = a.H, E = a.E;
-  const int cs = blockIdx.x / a.RS, rs = blockIdx.x % a.RS;
+  const int cs = rb / a.RS, rs = rb % a.RS;
   const int col = threadIdx.x & 31, rg = threadIdx.x >> 5;
   const int e = cs * kRouterCols + col;
   const int h0 = rs * kRH, nh = min(kRH, H - h0);
@@ -178,6 +181,18 @@ struct GroupSmem {
 };
 
 __device__ inline bool derive_group(const DecodeArgs& a, int q, GroupSmem& g, int& e_out, int& n_out) {
+  if (a.T == 1) {
+    // One token: its k experts are distinct, so every slot is its own group.
+    const int e = a.ids[q];
+    if (threadIdx.x == 0) {
+      g.pairs[0] = q;
+      g.toks[0] = 0;
+    }
+    __syncthreads();
+    e_out = e;
+    n_out = 1;
+    return (unsigned)e < (unsigned)a.E;
+  }
   const int P = a.T * a.k;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int e = a.ids[q];
@@ -206,99 +221,128 @@ __device__ inline bool derive_group(const DecodeArgs& a, int q, GroupSmem& g, in
   return true;
 }
 
-template <int RFMT, int SFMT>
+template <int RFMT>
 __global__ __launch_bounds__(256) void decode_gateup_kernel(DecodeArgs a) {
-  __shared__ union {
-    GemvSmem<1, 4, 2> g;
-    GemvSmem<4, 1, 1> d;
-  } sm;
+  __shared__ GemvSmem<1, 4, 2> sm;
   __shared__ GroupSmem grp;
   const int ntiles = a.I / gemv_rows_per_block<kOpGateUp>();
-  const int nrouted = a.T * a.k * ntiles;
-  if ((int)blockIdx.x < nrouted) {
-    const int q = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
-    int e, n;
-    if (!derive_group(a, q, grp, e, n)) return;
-    GemvIO io{a.x, a.h, nullptr, a.k, kInList, a.T};
-    gemv_tile<RFMT, kOpGateUp, 1, 4>(a.gate, a.up, io, GemvRows{e, 0, n, grp.toks, grp.pairs}, tile,
-                                     sm.g);
-  } else if constexpr (SFMT != 0) {  // shared expert down projection
-    GemvIO io{a.hs, a.ys, nullptr, a.k, kInShared, a.T};
-    gemv_tile<SFMT, kOpDown, 4, 1>(a.sd, a.sd, io, GemvRows{0, 0, a.T, nullptr, nullptr},
-                                   blockIdx.x - nrouted, sm.d);
-  }
-}
-
-template <int RFMT>
-__global__ __launch_bounds__(256) void decode_down_kernel(DecodeArgs a) {
-  __shared__ GemvSmem<4, 1, 1> sm;
-  __shared__ GroupSmem grp;
-  constexpr int RPB = gemv_rows_per_block<kOpDown>();
-  const int ntiles = (a.H + RPB - 1) / RPB;
   const int q = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
   int e, n;
   if (!derive_group(a, q, grp, e, n)) return;
-  GemvIO io{a.h, a.y, nullptr, a.k, kInList, a.T * a.k};
-  gemv_tile<RFMT, kOpDown, 4, 1>(a.down, a.down, io, GemvRows{e, 0, n, grp.pairs, grp.pairs}, tile,
-                                 sm);
+  GemvIO io{a.x, a.h, nullptr, a.k, kInList, a.T};
+  gemv_tile<RFMT, kOpGateUp, 1, 4>(a.gate, a.up, io, GemvRows{e, 0, n, grp.toks, grp.pairs}, tile,
+                                   sm);
 }
 
-// out[t] = bf16( sum_j w[t,j] * y[t*k+j] + y_shared[t] ), four columns per thread.
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  const int t = blockIdx.y;
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (n >= a.H) return;
-  f32x4 yv[kMaxTopK];
-  float wv[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < a.k) {
-      wv[j] = a.w[t * a.k + j];
-      yv[j] = *reinterpret_cast<const f32x4*>(a.y + (size_t)(t * a.k + j) * a.H + n);
-    }
-  }
-  f32x4 ys = (a.ys != nullptr) ? *reinterpret_cast<const f32x4*>(a.ys + (size_t)t * a.H + n)
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
+// One 16-row tile (weight rows n0..n0+15 of expert e) times one bf16 input
+// row of length K, for the calling wavefront.  The weights are decoded in
+// registers as in gemv_tile; the input row is the MFMA's B operand column 0.
+// Result: lane 16q holds output rows n0 + 4q + (0..3) (lanes with lane % 16
+// != 0 hold zeros).  Loads of four 128-wide chunks are issued together.
+template <int FMT>
+__device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const uint16_t* hrow,
+                                            int K) {
+  const int lane = __lane_id(), r = lane & 15, g = lane >> 4;
+  const int row = n0 + r;
+  const uint8_t* rp = w.codes + e * w.stride_codes + (size_t)row * row_bytes<FMT>(K);
+  const uint8_t* sp = scale_row_ptr<FMT>(w, e, row);
+  const uint16_t* brow = (r == 0) ? hrow : nullptr;
+  const int nch = (K + 127) / 128;
+  constexpr int D = 4;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < nch; cb += D) {
+    ARaw<FMT> ar[D];
+    u32x4 bx[D][4];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < a.k) {
+    for (int d = 0; d < D; ++d) ar[d] = load_a<FMT>(cb + d < nch ? rp : nullptr, sp, cb + d, g, K);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(wv[j], yv[j][q], acc[q]);
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bx[d][i] = load_b(cb + d < nch ? brow : nullptr, 128 * (cb + d) + 32 * g + 8 * i, K);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (cb + d >= nch) break;
+      f32x4 t = (FMT == FMT_FP8) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc;
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(ar[d]), as_bf16x8(bx[d][0]), t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(ar[d]), as_bf16x8(bx[d][1]), t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(ar[d]), as_bf16x8(bx[d][2]), t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(ar[d]), as_bf16x8(bx[d][3]), t, 0, 0, 0);
+      if constexpr (FMT == FMT_FP8)
+        acc = acc + ar[d].s * t;
+      else
+        acc = t;
     }
   }
-  acc = acc + ys;
-  *reinterpret_cast<uint2*>(a.out + (size_t)t * a.H + n) =
-      make_uint2(f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16),
-                 f32_to_bf16(acc[2]) | (uint32_t(f32_to_bf16(acc[3])) << 16));
+  return acc;
+}
+
+// Down projection of every routed slot of a token and of the shared expert,
+// combined in the same kernel: block (t, 16-column tile of H); wavefront w
+// takes slots w, w + 8, ... (slot k = the shared expert), writes its 16
+// outputs y_j to LDS, then out[t] = bf16(sum_j w_j * y_j + y_shared) in slot
+// order.  No per-pair y goes through memory.
+constexpr int kDcCols = 16;
+constexpr int kDcWaves = 8;
+
+template <int RFMT, int SFMT>
+__global__ __launch_bounds__(kDcWaves * kWave) void decode_down_combine_kernel(DecodeArgs a) {
+  __shared__ float yp[kMaxTopK + 1][kDcCols];
+  const int ntiles = a.H / kDcCols;
+  const int t = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+  const int n0 = tile * kDcCols;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int nslots = a.k + ((SFMT != 0) ? 1 : 0);
+  for (int j = wave; j < nslots; j += kDcWaves) {
+    f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (j < a.k) {
+      const int p = t * a.k + j;
+      const int e = a.ids[p];
+      if ((unsigned)e < (unsigned)a.E) {
+        y = gemv16_row<RFMT>(a.down, e, n0, a.h + (size_t)p * a.I, a.I);
+        if constexpr (RFMT == FMT_NVFP4) y = y * a.down.tscale[e];
+      }
+    } else if constexpr (SFMT != 0) {
+      y = gemv16_row<SFMT>(a.sd, 0, n0, a.hs + (size_t)t * a.I_shared, a.I_shared);
+      if constexpr (SFMT == FMT_NVFP4) y = y * a.sd.tscale[0];
+    }
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) yp[j][4 * (lane >> 4) + q] = y[q];
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < kDcCols) {
+    const int c = threadIdx.x;
+    float acc = 0.f;
+    for (int j = 0; j < a.k; ++j) acc = fmaf(a.w[t * a.k + j], yp[j][c], acc);
+    if constexpr (SFMT != 0) acc = acc + yp[a.k][c];
+    a.out[(size_t)t * a.H + n0 + c] = f32_to_bf16(acc);
+  }
 }
 
 template <int RFMT, int SFMT>
-hipError_t launch5(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
   const int nrb = a.RS * a.CS;
   const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
-  hipError_t err = launch(decode_router_kernel<SFMT>, dim3(nrb + nsg), dim3(256), 0, s, a);
+  hipError_t err = launch(decode_router_kernel<SFMT>, dim3(nsg + nrb), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
   err = launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
   if (err != hipSuccess) return err;
-  constexpr int RPD = gemv_rows_per_block<kOpDown>();
   const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
-  const int nsd = (SFMT != 0) ? (a.H + RPD - 1) / RPD : 0;
-  err = launch(decode_gateup_kernel<RFMT, SFMT>, dim3(ngu + nsd), dim3(256), 0, s, a);
+  err = launch(decode_gateup_kernel<RFMT>, dim3(ngu), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
-  const int nd = a.T * a.k * ((a.H + RPD - 1) / RPD);
-  err = launch(decode_down_kernel<RFMT>, dim3(nd), dim3(256), 0, s, a);
-  if (err != hipSuccess) return err;
-  return launch(decode_combine_kernel, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, s, a);
+  return launch(decode_down_combine_kernel<RFMT, SFMT>, dim3(a.T * (a.H / kDcCols)),
+                dim3(kDcWaves * kWave), 0, s, a);
 }
 
 template <int RFMT>
 hipError_t launch_r(int sfmt, const DecodeArgs& a, hipStream_t s) {
   switch (sfmt) {
-    case 0: return launch5<RFMT, 0>(a, s);
-    case FMT_NVFP4: return launch5<RFMT, FMT_NVFP4>(a, s);
-    case FMT_MXFP4: return launch5<RFMT, FMT_MXFP4>(a, s);
-    case FMT_FP8: return launch5<RFMT, FMT_FP8>(a, s);
+    case 0: return launch4<RFMT, 0>(a, s);
+    case FMT_NVFP4: return launch4<RFMT, FMT_NVFP4>(a, s);
+    case FMT_MXFP4: return launch4<RFMT, FMT_MXFP4>(a, s);
+    case FMT_FP8: return launch4<RFMT, FMT_FP8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

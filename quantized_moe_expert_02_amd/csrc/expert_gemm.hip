@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
           if (n >= N) continue;
           const float g = acc[r][c][j] * ts0;
           const float u = acc[r][c + 2][j] * ts1;
-          const float h = g / (1.0f + expf(-g)) * u;
+          const float h = silu_fast(g) * u;
           reinterpret_cast<uint16_t*>(p.out)[(size_t)orow * N + n] = f32_to_bf16(h);
         }
       } else {

@@ -316,8 +316,7 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
         for (int j = 0; j < 4; ++j) {
           const float gv = acc[0][j] * ts[0];
           const float uv = acc[1][j] * ts[1];
-          const float sg = gv / (1.0f + expf(-gv));
-          h[j] = f32_to_bf16(sg * uv);
+          h[j] = f32_to_bf16(silu_fast(gv) * uv);
         }
         uint16_t* o = reinterpret_cast<uint16_t*>(io.out) + (size_t)orow * N + nb;
         if (nb + 3 < N) {

@@ -419,8 +419,6 @@ int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T,
     a.w = w;
     a.h = at<uint16_t>(ws, p.h);
     a.hs = L->has_shared ? at<uint16_t>(ws, p.hs) : nullptr;
-    a.y = at<float>(ws, p.y);
-    a.ys = L->has_shared ? at<float>(ws, p.ys) : nullptr;
     a.out = out;
     return hip_status(launch_decode(a, s));
   }

@@ -43,6 +43,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// SiLU for the SwiGLU epilogues: g * sigmoid(g) with the hardware exp and
+// reciprocal (a few fp32 ulps, far below the bf16 rounding of h that
+// follows).  g = -inf gives NaN, +inf gives +inf, as g / (1 + exp(-g)) does.
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
 // Pack the upper halves of two floats that are exactly bf16-representable.
 __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);

@@ -124,8 +124,6 @@ struct DecodeArgs {
   float* w;           // [T][k]
   uint16_t* h;        // [T*k][I], row = pair t*k+j
   uint16_t* hs;       // [T][I_shared]
-  float* y;           // [T*k][H], row = pair t*k+j
-  float* ys;          // [T][H]
   uint16_t* out;      // [T][H]
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

@@ -230,6 +230,7 @@ struct BlockTopkSmem {
   uint64_t ckey[kMaxExperts];
   int crank[kMaxExperts];
   double dred[kTopkThreads / kWave];
+  uint32_t wthr[kTopkThreads / kWave];
   int ncand;
 };
 
@@ -248,49 +249,120 @@ __device__ __forceinline__ int ranks_before(uint64_t kf, int f, uint64_t ke, int
   return (kf > ke) | ((kf == ke) & (f < e));
 }
 
-// Writes the first `rounds` entries of the order into topv/topi/topc.  Two
-// levels: the rank of each expert among the 64 of its wavefront (keys
-// broadcast from registers with v_readlane), then the rank of the
-// wavefront-level survivors (rank < rounds) among themselves, the comparisons
-// split across the whole block.  Every member of the overall first `rounds`
-// survives its wavefront, and its rank among the survivors is its overall rank.
+// Coarse 32-bit key: the logit rounded to fp32 (a monotone map, so the k-th
+// largest coarse key is the coarse key of the k-th largest logit), in the
+// same class order as order_key.  Distinct logits may share a coarse key;
+// the exact order among candidates is taken on order_key afterwards.
+__device__ __forceinline__ uint32_t coarse_key(double v, bool excluded) {
+  if (excluded) return 0u;
+  if (v != v) return 1u;
+  float f = static_cast<float>(v);
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (u >> 31) ? ~u : (u | 0x80000000u);  // >= 0x007fffff (-inf) for every number
+}
+
+// Sum over the wavefront (DPP: within quads, half rows, rows, then across
+// rows with the row broadcasts); the total is returned to every lane.  Lanes
+// a broadcast step does not write add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_step(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float dpp_sum_f(float v) {
+  v = dpp_add_step<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add_step<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add_step<0x141, 0xf>(v);  // row_half_mirror
+  v = dpp_add_step<0x140, 0xf>(v);  // row_mirror
+  v = dpp_add_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_add_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// The `rounds`-th largest of the wavefront's coarse keys (ties counted), or 0
+// when fewer than `rounds` keys are nonzero: the largest t with
+// #{keys >= t} >= rounds, built one bit at a time from the top.
+template <int N>
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&c)[N], int rounds) {
+  uint32_t t = 0u;
+#pragma unroll 4
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) cnt += __popcll(__ballot(c[i] >= cand));
+    if (cnt >= rounds) t = cand;
+  }
+  return t;
+}
+
+// Writes the first `rounds` entries of the order into topv/topi/topc.
+// (1) Each wavefront finds its `rounds`-th largest coarse key, ties included.
+// (2) The largest of these per-wavefront values, thr, is at most the coarse
+//     key of the overall `rounds`-th entry (each wavefront alone has that
+//     many entries at or above its value), so every member of the overall
+//     first `rounds` has coarse key >= thr.
+// (3) The candidates (coarse key >= thr) are ranked exactly among themselves
+//     on order_key, the comparisons split across the block.
+// Needs E <= 2 * blockDim.x; the caller synchronises the block afterwards.
 __device__ inline void block_rank(BlockTopkSmem& sm, int E, int rounds) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int e0 = threadIdx.x, e1 = threadIdx.x + blockDim.x;
+  uint32_t c[2];
+  c[0] = (e0 < E) ? coarse_key(sm.v[e0], sm.excl[e0] != 0) : 0u;
+  c[1] = (e1 < E) ? coarse_key(sm.v[e1], sm.excl[e1] != 0) : 0u;
+  const uint32_t wt = wave_kth_key(c, rounds);
+  if (lane == 0) sm.wthr[wave] = wt;
   if (threadIdx.x == 0) sm.ncand = 0;
   __syncthreads();
-  for (int base = 0; base < E; base += blockDim.x) {
-    const int e = base + threadIdx.x;
-    const bool valid = e < E;
-    const uint64_t ke = valid ? order_key(sm.v[e], sm.excl[e] != 0) : 0ull;
-    const uint32_t klo = static_cast<uint32_t>(ke), khi = static_cast<uint32_t>(ke >> 32);
-    const int f0 = e & ~(kWave - 1);
-    int cnt = 0;
-#pragma unroll 16
-    for (int i = 0; i < kWave; ++i) {
-      // readlane returns int: widen through uint32_t (no sign extension)
-      const uint64_t ki =
-          (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(khi, i))) << 32) |
-          static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(klo, i)));
-      cnt += ranks_before(ki, f0 + i, ke, e);
-    }
-    if (valid && ke != 0ull && cnt < rounds) {
-      const int slot = atomicAdd(&sm.ncand, 1);
-      sm.cand[slot] = e;
-      sm.ckey[slot] = ke;
-      sm.crank[slot] = 0;
-    }
+  uint32_t thr = 0u;
+  for (int w = 0; w < nwaves; ++w) thr = max(thr, sm.wthr[w]);
+  if (thr == 0u) thr = 1u;  // fewer than `rounds` eligible in every wave: all eligible
+  // candidates, compacted per wavefront with one LDS atomic each
+  const bool q0 = c[0] >= thr, q1 = c[1] >= thr;
+  const uint64_t b0 = __ballot(q0), b1 = __ballot(q1);
+  const int n0 = __popcll(b0), n = n0 + __popcll(b1);
+  int base = 0;
+  if (lane == 0 && n > 0) base = atomicAdd(&sm.ncand, n);
+  base = __builtin_amdgcn_readfirstlane(base);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  if (q0) {
+    const int slot = base + __popcll(b0 & lt);
+    sm.cand[slot] = e0;
+    sm.ckey[slot] = order_key(sm.v[e0], false);
+    sm.crank[slot] = 0;
+  }
+  if (q1) {
+    const int slot = base + n0 + __popcll(b1 & lt);
+    sm.cand[slot] = e1;
+    sm.ckey[slot] = order_key(sm.v[e1], false);
+    sm.crank[slot] = 0;
   }
   __syncthreads();
   const int nc = sm.ncand;
-  const int segs = max(1, (int)blockDim.x / max(nc, 1));
-  const int len = (nc + segs - 1) / segs;
-  if ((int)threadIdx.x < nc * segs) {
-    const int i = threadIdx.x % nc, sgm = threadIdx.x / nc;
-    const int e = sm.cand[i];
-    const uint64_t ke = sm.ckey[i];
-    const int j1 = min(nc, (sgm + 1) * len);
-    int cnt = 0;
-    for (int j = sgm * len; j < j1; ++j) cnt += ranks_before(sm.ckey[j], sm.cand[j], ke, e);
-    if (cnt) atomicAdd(&sm.crank[i], cnt);
+  if (nc <= (int)blockDim.x) {
+    // each candidate's comparisons split over blockDim / nc threads
+    const int segs = max(1, (int)blockDim.x / max(nc, 1));
+    const int len = (nc + segs - 1) / segs;
+    if ((int)threadIdx.x < nc * segs) {
+      const int i = threadIdx.x % nc, sgm = threadIdx.x / nc;
+      const int e = sm.cand[i];
+      const uint64_t ke = sm.ckey[i];
+      const int j1 = min(nc, (sgm + 1) * len);
+      int cnt = 0;
+      for (int j = sgm * len; j < j1; ++j) cnt += ranks_before(sm.ckey[j], sm.cand[j], ke, e);
+      if (cnt) atomicAdd(&sm.crank[i], cnt);
+    }
+  } else {  // more candidates than threads (massive ties): each thread ranks several
+    for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+      const int e = sm.cand[i];
+      const uint64_t ke = sm.ckey[i];
+      int cnt = 0;
+      for (int j = 0; j < nc; ++j) cnt += ranks_before(sm.ckey[j], sm.cand[j], ke, e);
+      sm.crank[i] = cnt;
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nc; i += blockDim.x) {
@@ -360,27 +432,28 @@ __device__ inline void block_topk(BlockTopkSmem& sm, const BlockTopkArgs& a) {
       __syncthreads();
     }
   }
-  // Weights: softmax over the k selected (renormalised) or over all E.
+  // Weights: softmax over the k selected (renormalised) or over all E, in
+  // fp32 (the weights are fp32 outputs; the logit differences are taken in
+  // float64 first).
   const double v0 = sm.topv[0];
   if (!a.renorm) {
-    double part = 0.0;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) part += exp(sm.v[e] - v0);
-    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
+    float part = 0.f;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) part += expf(static_cast<float>(sm.v[e] - v0));
+    part = dpp_sum_f(part);
     if (lane == 0) sm.dred[wave] = part;
+    __syncthreads();
   }
-  __syncthreads();
   if (wave == 0) {
-    const double z = (lane < k) ? exp(sm.topv[lane] - v0) : 0.0;
-    double denom = 0.0;
+    const float z = (lane < k) ? expf(static_cast<float>(sm.topv[lane] - v0)) : 0.f;
+    float denom = 0.f;
     if (a.renorm) {
-      denom = z;
-      for (int m = 32; m >= 1; m >>= 1) denom += __shfl_xor(denom, m, kWave);
+      denom = dpp_sum_f(z);
     } else {
-      for (int i = 0; i < nwaves; ++i) denom += sm.dred[i];
+      for (int i = 0; i < nwaves; ++i) denom += static_cast<float>(sm.dred[i]);
     }
     if (lane < k) {
       a.ids[lane] = sm.topi[lane];
-      a.w[lane] = static_cast<float>(z / denom);
+      a.w[lane] = z / denom;
     }
   }
 }

@@ -144,14 +144,22 @@ def test_layer_is_deterministic(name):
         assert np.array_equal(u, v, equal_nan=True)
 
 
-def test_route_topk_given_logits_exact():
-    rng = np.random.default_rng(11)
-    T, E, k = 37, 64, 6
+@pytest.mark.parametrize("T,E,k", [(37, 64, 6), (9, 64, 6), (11, 1000, 12), (40, 300, 32)])
+def test_route_topk_given_logits_exact(T, E, k):
+    """Given logits: per-token block selection (T <= 16) and per-wavefront
+    selection (larger T), on ties, duplicates, NaN and infinities."""
+    rng = np.random.default_rng(11 + T)
     logits = rng.standard_normal((T, E)).astype(np.float32)
     logits[0, [5, 9, 40]] = 9.0
     logits[1, :] = 0.5
     logits[2, [1, 2]] = np.nan
     logits[3, 17] = np.inf
+    logits[4, :] = np.round(logits[4, :], 1)        # many exact duplicates
+    logits[5, ::2] = np.nan                          # half NaN
+    logits[6, :] = -np.inf
+    logits[6, 3] = -0.0
+    logits[6, 4] = 0.0
+    logits[7, :] = np.float32(1.0) + np.arange(E, dtype=np.float32) * np.float32(2**-23)
     w_ = synth.scaled(W["tiny_nvfp4_t4"], name="route", E=E, top_k=k)
     dl = device_layer(layer_for(w_))
     lg = torch.from_numpy(logits).cuda()
