@@ -10,8 +10,11 @@ captured HIP graph; inputs are resident in HBM before the timed region.
 Prints one JSON line.  `value` is tokens/s over the timed steps.  The
 `roofline` object covers the dominant kernel (the routed gate/up expert
 kernel): algorithmic bytes (decode, HBM-bound) or flops (prefill, MFMA-bound)
-per launch over its average launch duration, measured with HIP events
-bracketing each launch on the launch stream.  The
+per launch over its average launch duration, measured with one pair of HIP
+events around a batch of back-to-back launches on the launch stream;
+`traffic` is the counter-measured HBM bytes per launch from
+profiles/traffic_<workload>.json when those counters were taken on the
+current kernel sources (null otherwise).  The
 `cpu_baseline` object times the CPU oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -75,7 +78,16 @@ def main():
     ap.add_argument("--kernel-launches", type=int, default=192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for rocprofv3 --pmc runs: a plain copy of known size, then a few "
+                         "launches of the dominant kernel; no timing")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the FETCH_SIZE and WRITE_SIZE runs of --pmc-probe into "
+                         "profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.pmc_summarize:
+        pmc_summarize(args.workload, *args.pmc_summarize)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -119,6 +131,10 @@ def main():
     ref_route = O.route(x_bits, L.router_w, L.router_bias, L.top_k, L.renormalize)
     routing_exact = bool(np.array_equal(ids_np, ref_route.ids))
     log(f"[bench] routing matches the oracle: {routing_exact}")
+
+    if args.pmc_probe:
+        pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws)
+        return
 
     # graph of one pass over the weight sets
     def capture(n):
@@ -168,38 +184,33 @@ def main():
     # ---- dominant kernel: routed gate/up expert kernel, timed per launch ----
     E, k = L.E, L.top_k
     P = T * k
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    p2 = torch.empty(P, dtype=torch.int32, device=dev)
-    q2 = torch.empty(P, dtype=torch.int32, device=dev)
-    act = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    pws = torch.empty(moe.moe_permute_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
-    moe.moe_permute(ids, T, k, E, counts, offsets, p2, q2, act, pws)
-    h = torch.empty((P, L.I), dtype=torch.bfloat16, device=dev)
+    offsets, p2, act, h = dominant_inputs(moe, torch, dev, L, ids)
     M = args.kernel_launches
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(M)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(M)]
     for i in range(min(M, 2 * nsets)):  # warm
         moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, sets[i % nsets].desc, 0, offsets, p2, act, T,
                             x, h, ws)
     torch.cuda.synchronize()
+    # M launches back to back between one pair of events on the launch stream
+    # (the current stream); the average includes the dispatch gap between
+    # consecutive launches, which the profiler's per-kernel duration does not.
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
     if hasattr(torch.cuda, "_sleep"):
         torch.cuda._sleep(50_000_000)  # let the host queue every launch before the GPU reaches them
+    k0.record()
     for i in range(M):
-        starts[i].record()
         moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, sets[i % nsets].desc, 0, offsets, p2, act, T,
                             x, h, ws)
-        ends[i].record()
+    k1.record()
     torch.cuda.synchronize()
-    kt = sorted(s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends))
-    k_avg_us = sum(kt) / len(kt)
+    k_avg_us = k0.elapsed_time(k1) * 1e3 / M
     active = np.unique(ids_np)
     k_bytes = len(active) * (expert_bytes(L.gate) + expert_bytes(L.up)) + T * L.H * 2 + P * L.I * 2
     k_gbs = k_bytes / (k_avg_us * 1e-6) / 1e9
     k_flops = 2 * P * 2 * L.I * L.H
     k_tflops = k_flops / (k_avg_us * 1e-6) / 1e12
-    log(f"[bench] gate/up kernel: {k_avg_us:.2f} us avg over {M} launches "
-        f"(median {kt[len(kt) // 2]:.2f}), {k_bytes / 1e6:.2f} MB -> {k_gbs:.0f} GB/s, "
+    log(f"[bench] gate/up kernel: {k_avg_us:.2f} us avg over {M} back-to-back launches, "
+        f"{k_bytes / 1e6:.2f} MB -> {k_gbs:.0f} GB/s, "
         f"{k_tflops:.1f} TFLOP/s")
     if T <= GEMV_MAX_ROWS:
         # weights streamed once per group: bound by HBM
@@ -243,13 +254,134 @@ def main():
         "layer_fp4_mfma_frac": round(layer_tflops / FP4_PEAK_TFLOPS, 5),
         "unique_experts": int(len(active)),
         "routing_matches_oracle": routing_exact,
-        "roofline": roof,
+        "roofline": dict(roof, traffic=load_traffic(w.name, T)),
     }
 
     # ---- CPU baseline: the oracle on a bounded sample ----
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, L, x_bits, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def dominant_inputs(moe, torch, dev, L, ids):
+    """Grouping of the routed pairs for standalone launches of the routed
+    gate/up kernel (the layer's dominant kernel)."""
+    T, k, E = ids.shape[0], L.top_k, L.E
+    P = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    p2 = torch.empty(P, dtype=torch.int32, device=dev)
+    q2 = torch.empty(P, dtype=torch.int32, device=dev)
+    act = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pws = torch.empty(moe.moe_permute_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+    moe.moe_permute(ids, T, k, E, counts, offsets, p2, q2, act, pws)
+    h = torch.empty((P, L.I), dtype=torch.bfloat16, device=dev)
+    return offsets, p2, act, h
+
+
+PMC_COPY_BYTES = 256 << 20
+PMC_COPIES = 4
+PMC_LAUNCHES = 8
+
+
+def pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws):
+    """Dispatches for a counter run: PMC_COPIES plain copies of PMC_COPY_BYTES
+    (x * 1 into another buffer; the calibration: bytes per counted KiB), then
+    PMC_LAUNCHES launches of
+    the dominant kernel, cycling weight sets as the timed run does."""
+    T = ids.shape[0]
+    offsets, p2, act, h = dominant_inputs(moe, torch, dev, L, ids)
+    src = torch.ones(PMC_COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(PMC_COPIES):  # an elementwise kernel that reads and writes every byte once
+        torch.mul(src, 1, out=dst)
+    torch.cuda.synchronize()
+    for i in range(PMC_LAUNCHES):
+        moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, sets[(i + 1) % nsets].desc, 0, offsets, p2,
+                            act, T, x, h, ws)
+    torch.cuda.synchronize()
+    log(f"[bench] pmc probe: {PMC_COPIES} copies of {PMC_COPY_BYTES} B, "
+        f"{PMC_LAUNCHES} dominant-kernel launches")
+
+
+def dominant_kernel_name(w):
+    """Template instance of the routed gate/up kernel for the workload."""
+    fmt = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3}[w.fmt]
+    base = "expert_gemv_kernel" if w.T <= GEMV_MAX_ROWS else "grouped_gemm_kernel"
+    return f"{base}<{fmt}, 0>"
+
+
+def dominant_sources(T):
+    pkg = os.path.join(ROOT, "quantized_moe_expert_02_amd", "csrc")
+    files = ["moe_device.cuh", "gemv_core.cuh"]
+    files += ["expert_gemv.hip"] if T <= GEMV_MAX_ROWS else ["expert_gemm.hip"]
+    return [os.path.join(pkg, f) for f in files]
+
+
+def source_hash(T):
+    import hashlib
+    hsh = hashlib.sha256()
+    for f in dominant_sources(T):
+        with open(f, "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def load_traffic(workload, T):
+    """Counter-measured HBM bytes per launch of the dominant kernel, if the
+    counters were taken on the kernel sources as they are now; else None."""
+    p = traffic_path(workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash(T):
+        return None
+    return t["bytes_per_launch"]
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def pmc_summarize(workload, fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the --pmc-probe runs,
+    scaled by what the same counter reads for the plain copy (which moves
+    PMC_COPY_BYTES each way), averaged over the dominant kernel's launches."""
+    w = __import__("synth").WORKLOADS[workload]
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _pmc_rows(d) if r.get("Counter_Name", r.get("Counter-Name")) == name]
+        val = lambda r: float(r.get("Counter_Value", r.get("Counter-Value")))  # noqa: E731
+        copy = [val(r) for r in rows if "elementwise" in r["Kernel_Name"]
+                and "Fill" not in r["Kernel_Name"]]
+        kname = dominant_kernel_name(w)
+        kern = [val(r) for r in rows if r["Kernel_Name"].startswith("void moe::(anonymous namespace)::" + kname)]
+        kern = kern[-PMC_LAUNCHES:]  # the probe's own launches come last
+        if not copy or not kern:
+            raise SystemExit(f"{name}: no copy or kernel dispatches in {d}")
+        kib_copy = sorted(copy)[len(copy) // 2]
+        factor = PMC_COPY_BYTES / kib_copy       # bytes per counted KiB
+        out[name] = {"copy_kib": kib_copy, "bytes_per_kib": factor,
+                     "kernel_kib_avg": sum(kern) / len(kern), "launches": len(kern),
+                     "kernel_bytes_avg": factor * sum(kern) / len(kern)}
+    res = {"workload": workload, "kernel": dominant_kernel_name(w), "source_hash": source_hash(w.T),
+           "bytes_per_launch": round(out["FETCH_SIZE"]["kernel_bytes_avg"]
+                                     + out["WRITE_SIZE"]["kernel_bytes_avg"]),
+           "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"]}
+    with open(traffic_path(workload), "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
 
 
 def cpu_baseline(w, L, x_bits, budget_s):
