@@ -160,6 +160,7 @@ constexpr int kWaveTopkTokens = 4;
 
 __global__ __launch_bounds__(kWave * kWaveTopkTokens) void topk_wave_kernel(TopkArgs a) {
   __shared__ double vals[kWaveTopkTokens][kMaxExperts];
+  __shared__ WaveTopkScratch scratch[kWaveTopkTokens];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kWaveTopkTokens + wave;
   if (t >= a.T) return;
@@ -199,6 +200,7 @@ __global__ __launch_bounds__(kWave * kWaveTopkTokens) void topk_wave_kernel(Topk
   tk.ids = a.ids + (size_t)t * a.k;
   tk.w = a.w + (size_t)t * a.k;
   tk.recomputed = a.recomputed ? a.recomputed + t : nullptr;
+  tk.sc = &scratch[wave];
   wave_topk(tk);
 }
 

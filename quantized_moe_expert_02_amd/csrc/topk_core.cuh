@@ -110,6 +110,7 @@ struct TopkToken {
   int* ids;            // [k] out
   float* w;            // [k] out
   int* recomputed;     // out flag or nullptr
+  struct WaveTopkScratch* sc;  // LDS scratch of this wavefront
 };
 
 // Lanes r < rounds hold the r-th selected entry in (top_v, top_i, top_c).
@@ -153,64 +154,6 @@ __device__ inline int wave_select(const double* vals, int E, uint32_t excl, int 
     ++got;
   }
   return got;
-}
-
-// Select, certify (optionally recompute), and write ids and weights.
-__device__ inline void wave_topk(const TopkToken& a) {
-  const int lane = __lane_id();
-  const int E = a.E, k = a.k;
-  const int K1 = (k + 1 <= E) ? k + 1 : k;
-  double top_v = 0.0;
-  int top_i = 0, top_c = 0;
-  uint32_t excl = 0;  // bit i: expert lane + 64*i not eligible (after a recompute)
-  int got = wave_select(a.vals, E, 0u, a.certify ? K1 : k, top_v, top_i, top_c);
-  if (a.certify) {
-    const double next_v = __shfl_down(top_v, 1, kWave);
-    const bool fin_r = (lane >= got) || (top_c == 2 && (top_v - top_v == 0.0));
-    const bool finite = __all(fin_r);
-    const bool gap_ok = (lane + 1 >= got) || (top_v - next_v > 2.0 * a.bound);
-    const bool ok = (got == K1) && finite && __all(gap_ok);
-    if (a.recomputed != nullptr && lane == 0) *a.recomputed = ok ? 0 : 1;
-    if (!ok) {
-      // Every exact top-k member has a fast logit >= (k-th fast value) - 2*bound.
-      // A non-finite value among the top k+1 or a non-finite bound says
-      // nothing about the others: then every logit is recomputed.
-      const bool all = !finite || !(a.bound < __builtin_inf());
-      const double thr = __shfl(top_v, k - 1, kWave) - 2.0 * a.bound;
-      const int nper = (E + kWave - 1) / kWave;
-      for (int i = 0; i < nper; ++i) {
-        const int e = lane + kWave * i;
-        const double v = (e < E) ? a.vals[e] : 0.0;
-        const bool cand = (e < E) && (all || (v == v && v >= thr));
-        if (e < E && !cand) excl |= 1u << i;
-        uint64_t mask = __ballot(cand);
-        while (mask) {
-          const int l = __builtin_ctzll(mask);
-          mask &= mask - 1;
-          const double val = dd_logit(a.xrow, a.wr, a.wr_sh, a.wr_se, a.H, l + kWave * i, a.bias);
-          if (lane == 0) a.vals[l + kWave * i] = val;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      got = wave_select(a.vals, E, excl, k, top_v, top_i, top_c);
-    }
-  }
-  // Weights: softmax over the k selected (renormalised) or over all E.
-  const double v0 = __shfl(top_v, 0, kWave);
-  double z = (lane < k) ? exp(top_v - v0) : 0.0;
-  double denom;
-  if (a.renorm) {
-    denom = z;
-  } else {
-    denom = 0.0;
-    for (int e = lane; e < E; e += kWave) denom += exp(a.vals[e] - v0);
-  }
-  for (int m = 32; m >= 1; m >>= 1) denom += __shfl_xor(denom, m, kWave);
-  if (lane < k) {
-    a.ids[lane] = top_i;
-    a.w[lane] = static_cast<float>(z / denom);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -455,6 +398,174 @@ __device__ inline void block_topk(BlockTopkSmem& sm, const BlockTopkArgs& a) {
       a.ids[lane] = sm.topi[lane];
       a.w[lane] = z / denom;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront-per-token top-k (large batches): the same selection as block_rank
+// inside one wavefront (up to 16 logits per lane).
+// ---------------------------------------------------------------------------
+struct WaveTopkScratch {
+  int cand[kWave];
+  uint64_t ckey[kWave];
+  double tv[kMaxTopK + 1];
+  int ti[kMaxTopK + 1];
+  int tc[kMaxTopK + 1];
+  unsigned char mark[kMaxExperts];  // 1: logit to recompute
+};
+
+constexpr int kMaxPerLane = kMaxExperts / kWave;
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Lanes r < rounds receive the r-th entry of the order in (top_v, top_i,
+// top_c); returns how many entries exist (eligible logits, at most rounds).
+// The `rounds`-th largest fp32-rounded key is found by bisection; the
+// candidates at or above it (at most 64, else the round-by-round selection
+// takes over) are ranked exactly on order_key.
+__device__ inline int wave_rank_select(const double* vals, int E, uint32_t excl, int rounds,
+                                       WaveTopkScratch& sc, double& top_v, int& top_i, int& top_c) {
+  const int lane = __lane_id();
+  const int nper = (E + kWave - 1) / kWave;
+  uint32_t c[kMaxPerLane];
+  int elig = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + kWave * i;
+    c[i] = (i < nper && e < E) ? coarse_key(vals[e], (excl >> i) & 1u) : 0u;
+    if (i < nper) elig += __popcll(__ballot(c[i] != 0u));
+  }
+  uint32_t t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i)
+      if (i < nper) cnt += __popcll(__ballot(c[i] >= cand));
+    if (cnt >= rounds) t = cand;
+  }
+  if (t == 0u) t = 1u;  // fewer than `rounds` eligible: every eligible logit
+  int nc = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i)
+    if (i < nper) nc += __popcll(__ballot(c[i] >= t));
+  if (nc > kWave) return wave_select(vals, E, excl, rounds, top_v, top_i, top_c);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    if (i >= nper) break;
+    const bool q = c[i] >= t;
+    const uint64_t b = __ballot(q);
+    if (q) {
+      const int slot = base + __popcll(b & lt);
+      const int e = lane + kWave * i;
+      sc.cand[slot] = e;
+      sc.ckey[slot] = order_key(vals[e], false);
+    }
+    base += __popcll(b);
+  }
+  wave_lds_sync();
+  if (lane < nc) {
+    const int e = sc.cand[lane];
+    const uint64_t ke = sc.ckey[lane];
+    int cnt = 0;
+    for (int j = 0; j < nc; ++j) cnt += ranks_before(sc.ckey[j], sc.cand[j], ke, e);
+    if (cnt < rounds) {
+      sc.tv[cnt] = vals[e];
+      sc.ti[cnt] = e;
+      sc.tc[cnt] = (ke == 1ull) ? 1 : 2;
+    }
+  }
+  wave_lds_sync();
+  const int got = min(rounds, elig);
+  if (lane < got) {
+    top_v = sc.tv[lane];
+    top_i = sc.ti[lane];
+    top_c = sc.tc[lane];
+  }
+  wave_lds_sync();
+  return got;
+}
+
+// Select, certify (optionally recompute), and write ids and weights.
+__device__ inline void wave_topk(const TopkToken& a) {
+  const int lane = __lane_id();
+  const int E = a.E, k = a.k;
+  const int K1 = (k + 1 <= E) ? k + 1 : k;
+  double top_v = 0.0;
+  int top_i = 0, top_c = 0;
+  uint32_t excl = 0;  // bit i: expert lane + 64*i not eligible (after a recompute)
+  int got = wave_rank_select(a.vals, E, 0u, a.certify ? K1 : k, *a.sc, top_v, top_i, top_c);
+  if (a.certify) {
+    const double next_v = __shfl_down(top_v, 1, kWave);
+    const bool fin_r = (lane >= got) || (top_c == 2 && (top_v - top_v == 0.0));
+    const bool finite = __all(fin_r);
+    const bool gap_ok = (lane + 1 >= got) || (top_v - next_v > 2.0 * a.bound);
+    const bool ok = (got == K1) && finite && __all(gap_ok);
+    if (a.recomputed != nullptr && lane == 0) *a.recomputed = ok ? 0 : 1;
+    if (!ok) {
+      // Exact logits are needed only where the fast order is in doubt: the
+      // members of close pairs (gap <= 2*bound) among the first k, and, when
+      // the k-th and (k+1)-th are close, every logit within 2*bound of the
+      // k-th.  Any other logit is more than 2*bound from all of those, so its
+      // fast value orders it correctly against their exact values and the
+      // selection is rerun on the mixed values.  A non-finite value among
+      // the top k+1 or a non-finite bound says nothing: recompute all.
+      const bool all = !finite || !(a.bound < __builtin_inf());
+      const double two_b = 2.0 * a.bound;
+      const bool close_r = (lane + 1 < got) && !(top_v - next_v > two_b);
+      // (every lane runs the shuffle: a lane that reads from an inactive lane
+      // gets 0)
+      const int close_up = __shfl_up(close_r ? 1 : 0, 1, kWave);
+      const bool close_prev = (lane > 0) && close_up != 0;
+      const bool boundary = __shfl(close_r ? 1 : 0, k - 1, kWave) != 0;
+      const double thr = __shfl(top_v, k - 1, kWave) - two_b;
+      const int nper = (E + kWave - 1) / kWave;
+      WaveTopkScratch& sc = *a.sc;
+      for (int i = 0; i < nper; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E) sc.mark[e] = 0;
+      }
+      wave_lds_sync();
+      if (lane < k && lane < got && (close_r || close_prev)) sc.mark[top_i] = 1;
+      wave_lds_sync();
+      for (int i = 0; i < nper; ++i) {
+        const int e = lane + kWave * i;
+        const double v = (e < E) ? a.vals[e] : 0.0;
+        const bool cand =
+            (e < E) && (all || sc.mark[e] != 0 || (boundary && v == v && v >= thr));
+        uint64_t mask = __ballot(cand);
+        while (mask) {
+          const int l = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          const double val = dd_logit(a.xrow, a.wr, a.wr_sh, a.wr_se, a.H, l + kWave * i, a.bias);
+          if (lane == 0) a.vals[l + kWave * i] = val;
+        }
+      }
+      wave_lds_sync();
+      got = wave_rank_select(a.vals, E, excl, k, *a.sc, top_v, top_i, top_c);
+    }
+  }
+  // Weights: softmax over the k selected (renormalised) or over all E, in
+  // fp32 (the logit differences are taken in float64 first).
+  const double v0 = __shfl(top_v, 0, kWave);
+  const float z = (lane < k) ? expf(static_cast<float>(top_v - v0)) : 0.f;
+  float denom;
+  if (a.renorm) {
+    denom = dpp_sum_f(z);
+  } else {
+    float part = 0.f;
+    for (int e = lane; e < E; e += kWave) part += expf(static_cast<float>(a.vals[e] - v0));
+    denom = dpp_sum_f(part);
+  }
+  if (lane < k) {
+    a.ids[lane] = top_i;
+    a.w[lane] = z / denom;
   }
 }
 
