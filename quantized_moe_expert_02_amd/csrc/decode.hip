@@ -8,16 +8,15 @@
 // (an L2 write-back) and costs far more; so the layer runs as four short
 // launches with no intra-kernel hand-off:
 //
-//   1. router partial sums over (128-row slice x 32 experts) blocks; the
-//      first blocks compute the shared expert's gate/up + SwiGLU (it does not
-//      depend on routing);
+//   1. router partial sums over (128-row slice x 32 experts) blocks;
 //   2. one block per token: sum the slices, select the top-k (coarse
 //      threshold, then exact ranking of the candidates), certify it against
 //      the exact logits (recomputing near ties), weights;
 //   3. each active routed expert's gate/up + SwiGLU, its weights streamed once
 //      for all of its tokens (blocks are laid out per routed pair slot; the
 //      block of an expert's first pair derives the expert's (token, slot)
-//      pairs from the <= 256 routed ids, the others exit);
+//      pairs from the <= 256 routed ids, the others exit); the first blocks
+//      compute the shared expert's gate/up + SwiGLU;
 //   4. per (token, 16 output columns): the down projections of the token's k
 //      slots and of the shared expert, combined in slot order in fp32 and
 //      rounded once to bf16.
@@ -40,24 +39,9 @@ struct RouterSmem {
   float reda[8][kTmax][kRouterCols];
 };
 
-template <int SFMT>
 __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
-  __shared__ union {
-    RouterSmem r;
-    GemvSmem<GemvShape<kOpGateUp>::WN, GemvShape<kOpGateUp>::WK, 2> g;
-  } sm;
-  // The shared expert's blocks come first: they do the most work, so they
-  // should be dispatched first.
-  const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
-  if ((int)blockIdx.x < nsg) {  // shared expert gate/up + SwiGLU
-    if constexpr (SFMT != 0) {
-      GemvIO io{a.x, a.hs, nullptr, a.k, kInShared, a.T};
-      gemv_tile<SFMT, kOpGateUp, 1, 4>(a.sg, a.su, io, GemvRows{0, 0, a.T, nullptr, nullptr},
-                                       blockIdx.x, sm.g);
-    }
-    return;
-  }
-  const int rb = blockIdx.x - nsg;
+  __shared__ RouterSmem sm;
+  const int rb = blockIdx.x;
   const int T = a.T, H = a.H, E = a.E;
   const int cs = rb / a.RS, rs = rb % a.RS;
   const int col = threadIdx.x & 31, rg = threadIdx.x >> 5;
@@ -73,7 +57,7 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
   }
   for (int i = threadIdx.x; i < kTmax * kRH; i += 256) {
     const int t = i / kRH, h = i % kRH;
-    sm.r.xs[t][h] = (t < T && h < nh) ? bf16_to_f32(a.x[(size_t)t * H + h0 + h]) : 0.f;
+    sm.xs[t][h] = (t < T && h < nh) ? bf16_to_f32(a.x[(size_t)t * H + h0 + h]) : 0.f;
   }
   __syncthreads();
   double acc[kTmax];
@@ -91,15 +75,15 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < kTmax; ++t) {
       if (t < T) {  // bf16 * fp32 is exact in float64
-        acc[t] = fma(static_cast<double>(sm.r.xs[t][h]), wd, acc[t]);
-        aa[t] = fmaf(fabsf(sm.r.xs[t][h]), wa, aa[t]);
+        acc[t] = fma(static_cast<double>(sm.xs[t][h]), wd, acc[t]);
+        aa[t] = fmaf(fabsf(sm.xs[t][h]), wa, aa[t]);
       }
     }
   }
 #pragma unroll
   for (int t = 0; t < kTmax; ++t) {
-    sm.r.red[rg][t][col] = acc[t];
-    sm.r.reda[rg][t][col] = aa[t];
+    sm.red[rg][t][col] = acc[t];
+    sm.reda[rg][t][col] = aa[t];
   }
   __syncthreads();
   if (rg < T && e < E) {  // thread (t = rg, col) folds the 8 row groups
@@ -107,8 +91,8 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
     double s = 0.0;
     float av = 0.f;
     for (int g = 0; g < 8; ++g) {
-      s += sm.r.red[g][t][col];
-      av += sm.r.reda[g][t][col];
+      s += sm.red[g][t][col];
+      av += sm.reda[g][t][col];
     }
     a.part[((size_t)rs * T + t) * E + e] = static_cast<float>(s);
     a.apart[((size_t)rs * T + t) * E + e] = av;
@@ -221,12 +205,23 @@ __device__ inline bool derive_group(const DecodeArgs& a, int q, GroupSmem& g, in
   return true;
 }
 
-template <int RFMT>
+template <int RFMT, int SFMT>
 __global__ __launch_bounds__(256) void decode_gateup_kernel(DecodeArgs a) {
   __shared__ GemvSmem<1, 4, 2> sm;
   __shared__ GroupSmem grp;
+  // The shared expert's gate/up blocks (independent of routing) come first.
+  const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
+  if ((int)blockIdx.x < nsg) {
+    if constexpr (SFMT != 0) {
+      GemvIO io{a.x, a.hs, nullptr, a.k, kInShared, a.T};
+      gemv_tile<SFMT, kOpGateUp, 1, 4>(a.sg, a.su, io, GemvRows{0, 0, a.T, nullptr, nullptr},
+                                       blockIdx.x, sm);
+    }
+    return;
+  }
   const int ntiles = a.I / gemv_rows_per_block<kOpGateUp>();
-  const int q = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+  const int b = blockIdx.x - nsg;
+  const int q = b / ntiles, tile = b % ntiles;
   int e, n;
   if (!derive_group(a, q, grp, e, n)) return;
   GemvIO io{a.x, a.h, nullptr, a.k, kInList, a.T};
@@ -325,12 +320,12 @@ template <int RFMT, int SFMT>
 hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
   const int nrb = a.RS * a.CS;
   const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
-  hipError_t err = launch(decode_router_kernel<SFMT>, dim3(nsg + nrb), dim3(256), 0, s, a);
+  hipError_t err = launch(decode_router_kernel, dim3(nrb), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
   err = launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
   if (err != hipSuccess) return err;
   const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
-  err = launch(decode_gateup_kernel<RFMT>, dim3(ngu), dim3(256), 0, s, a);
+  err = launch(decode_gateup_kernel<RFMT, SFMT>, dim3(nsg + ngu), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;
   return launch(decode_down_combine_kernel<RFMT, SFMT>, dim3(a.T * (a.H / kDcCols)),
                 dim3(kDcWaves * kWave), 0, s, a);

@@ -217,39 +217,43 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
       tmp[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+  // 16-row MFMA tiles of this wave that hold rows of the group (a short
+  // group's tile is mostly padding: skip the padding's MFMAs and reads)
+  const int vrows = m1 - m0 - 64 * wm;
+  const int vr = vrows <= 0 ? 0 : min(4, (vrows + 15) / 16);
   const int nk = (K + BK - 1) / BK;
-  Stage<FMT> st;
-  load_stage(0, st);
-  store_stage(0, st);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) load_stage((ks + 1) * BK, st);
+
+  // MFMAs of step ks on LDS buffer buf, and (FP8) the 128-wide K block close.
+  auto compute_step = [&](int buf, int ks) {
+    if (vr > 0) {
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8 af[4], bfr[4];
-      const int ko = kk + 8 * (lane >> 4);
+      for (int kk = 0; kk < BK; kk += 32) {
+        bf16x8 af[4], bfr[4];
+        const int ko = kk + 8 * (lane >> 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        af[r] = *reinterpret_cast<const bf16x8*>(&sm.a[buf][64 * wm + 16 * r + (lane & 15)][ko]);
+        for (int c = 0; c < 4; ++c)
+          bfr[c] = *reinterpret_cast<const bf16x8*>(&sm.b[buf][bcol[c] + (lane & 15)][ko]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        bfr[c] = *reinterpret_cast<const bf16x8*>(&sm.b[buf][bcol[c] + (lane & 15)][ko]);
+        for (int r = 0; r < 4; ++r)
+          if (r < vr)
+            af[r] = *reinterpret_cast<const bf16x8*>(&sm.a[buf][64 * wm + 16 * r + (lane & 15)][ko]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r) {
+          if (r >= vr) continue;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if constexpr (FMT == FMT_FP8)
-            tmp[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[c], tmp[r][c], 0, 0, 0);
-          else
-            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[c], acc[r][c], 0, 0, 0);
+          for (int c = 0; c < 4; ++c) {
+            if constexpr (FMT == FMT_FP8)
+              tmp[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[c], tmp[r][c], 0, 0, 0);
+            else
+              acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[c], acc[r][c], 0, 0, 0);
+          }
         }
+      }
     }
     if constexpr (FMT == FMT_FP8) {
       // close a 128-wide K block: acc += s(block) * partial
       const int kend = (ks + 1) * BK;
-      if ((kend % 128) == 0 || !more) {
+      if ((kend % 128) == 0 || ks + 1 == nk) {
         const int kblk = (ks * BK) / 128;
         const int cb = (K + 127) / 128;
 #pragma unroll
@@ -270,7 +274,33 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
         }
       }
     }
-    if (more) store_stage(buf ^ 1, st);
+  };
+
+  // Two register stages in flight: while step ks is computed from LDS, the
+  // global loads of steps ks+1 and ks+2 are outstanding, so each load has two
+  // compute steps to arrive.  The loop is unrolled by two so that the
+  // stages keep static register names.
+  Stage<FMT> s0, s1;
+  load_stage(0, s0);
+  store_stage(0, s0);
+  if (nk > 1) load_stage(BK, s0);
+  if (nk > 2) load_stage(2 * BK, s1);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ks += 2) {
+    // step ks on buffer 0; s0 holds step ks+1, s1 holds step ks+2
+    compute_step(0, ks);
+    if (ks + 1 < nk) {
+      store_stage(1, s0);
+      if (ks + 3 < nk) load_stage((ks + 3) * BK, s0);
+    }
+    __syncthreads();
+    if (ks + 1 >= nk) break;
+    // step ks+1 on buffer 1; s1 holds step ks+2, s0 holds step ks+3
+    compute_step(1, ks + 1);
+    if (ks + 2 < nk) {
+      store_stage(0, s1);
+      if (ks + 4 < nk) load_stage((ks + 4) * BK, s1);
+    }
     __syncthreads();
   }
 

@@ -256,7 +256,13 @@ __device__ inline void block_rank(BlockTopkSmem& sm, int E, int rounds) {
   uint32_t c[2];
   c[0] = (e0 < E) ? coarse_key(sm.v[e0], sm.excl[e0] != 0) : 0u;
   c[1] = (e1 < E) ? coarse_key(sm.v[e1], sm.excl[e1] != 0) : 0u;
-  const uint32_t wt = wave_kth_key(c, rounds);
+  uint32_t wt;
+  if (E > (int)blockDim.x) {
+    wt = wave_kth_key(c, rounds);
+  } else {  // one logit per thread
+    const uint32_t c1[1] = {c[0]};
+    wt = wave_kth_key(c1, rounds);
+  }
   if (lane == 0) sm.wthr[wave] = wt;
   if (threadIdx.x == 0) sm.ncand = 0;
   __syncthreads();
