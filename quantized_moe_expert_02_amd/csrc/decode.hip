@@ -205,17 +205,19 @@ __device__ inline bool derive_group(const DecodeArgs& a, int q, GroupSmem& g, in
   return true;
 }
 
+constexpr int kGuWK = GemvShape<kOpGateUp>::WK;  // K split of the gate/up tiles
+
 template <int RFMT, int SFMT>
-__global__ __launch_bounds__(256) void decode_gateup_kernel(DecodeArgs a) {
-  __shared__ GemvSmem<1, 4, 2> sm;
+__global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs a) {
+  __shared__ GemvSmem<1, kGuWK, 2> sm;
   __shared__ GroupSmem grp;
   // The shared expert's gate/up blocks (independent of routing) come first.
   const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
   if ((int)blockIdx.x < nsg) {
     if constexpr (SFMT != 0) {
       GemvIO io{a.x, a.hs, nullptr, a.k, kInShared, a.T};
-      gemv_tile<SFMT, kOpGateUp, 1, 4>(a.sg, a.su, io, GemvRows{0, 0, a.T, nullptr, nullptr},
-                                       blockIdx.x, sm);
+      gemv_tile<SFMT, kOpGateUp, 1, kGuWK>(a.sg, a.su, io, GemvRows{0, 0, a.T, nullptr, nullptr},
+                                           blockIdx.x, sm);
     }
     return;
   }
@@ -225,8 +227,8 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DecodeArgs a) {
   int e, n;
   if (!derive_group(a, q, grp, e, n)) return;
   GemvIO io{a.x, a.h, nullptr, a.k, kInList, a.T};
-  gemv_tile<RFMT, kOpGateUp, 1, 4>(a.gate, a.up, io, GemvRows{e, 0, n, grp.toks, grp.pairs}, tile,
-                                   sm);
+  gemv_tile<RFMT, kOpGateUp, 1, kGuWK>(a.gate, a.up, io, GemvRows{e, 0, n, grp.toks, grp.pairs},
+                                       tile, sm);
 }
 
 // One 16-row tile (weight rows n0..n0+15 of expert e) times one bf16 input
@@ -273,22 +275,24 @@ __device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const
 }
 
 // Down projection of every routed slot of a token and of the shared expert,
-// combined in the same kernel: block (t, 16-column tile of H); wavefront w
-// takes slots w, w + 8, ... (slot k = the shared expert), writes its 16
+// combined in the same kernel: block (t, 16-column tile of H) of one
+// wavefront per slot (at most 16; wavefront w takes slots w, w + 16, ...;
+// slot k = the shared expert), each writes its 16
 // outputs y_j to LDS, then out[t] = bf16(sum_j w_j * y_j + y_shared) in slot
 // order.  No per-pair y goes through memory.
 constexpr int kDcCols = 16;
-constexpr int kDcWaves = 8;
+constexpr int kDcMaxWaves = 16;  // one wavefront per slot up to 16 slots
 
 template <int RFMT, int SFMT>
-__global__ __launch_bounds__(kDcWaves * kWave) void decode_down_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDcMaxWaves * kWave) void decode_down_combine_kernel(DecodeArgs a) {
   __shared__ float yp[kMaxTopK + 1][kDcCols];
   const int ntiles = a.H / kDcCols;
   const int t = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
   const int n0 = tile * kDcCols;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nslots = a.k + ((SFMT != 0) ? 1 : 0);
-  for (int j = wave; j < nslots; j += kDcWaves) {
+  const int nwaves = blockDim.x / kWave;
+  for (int j = wave; j < nslots; j += nwaves) {
     f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
     if (j < a.k) {
       const int p = t * a.k + j;
@@ -325,10 +329,16 @@ hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
   err = launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
   if (err != hipSuccess) return err;
   const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
-  err = launch(decode_gateup_kernel<RFMT, SFMT>, dim3(nsg + ngu), dim3(256), 0, s, a);
+  err = launch(decode_gateup_kernel<RFMT, SFMT>, dim3(nsg + ngu), dim3(kWave * kGuWK), 0, s, a);
   if (err != hipSuccess) return err;
+  // One wavefront per slot (one round trip per block) when the grid is
+  // smaller than the GPU; otherwise 8 per block keep more blocks resident.
+  const int nslots = a.k + ((SFMT != 0) ? 1 : 0);
+  const int nblocks = a.T * (a.H / kDcCols);
+  const int dcw = (nblocks < 256) ? (nslots < kDcMaxWaves ? nslots : kDcMaxWaves)
+                                  : (nslots < 8 ? nslots : 8);
   return launch(decode_down_combine_kernel<RFMT, SFMT>, dim3(a.T * (a.H / kDcCols)),
-                dim3(kDcWaves * kWave), 0, s, a);
+                dim3(dcw * kWave), 0, s, a);
 }
 
 template <int RFMT>

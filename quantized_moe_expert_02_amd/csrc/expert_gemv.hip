@@ -14,7 +14,7 @@ struct GemvKParams {
 };
 
 template <int FMT, int OP>
-__global__ __launch_bounds__(256) void expert_gemv_kernel(GemvKParams p) {
+__global__ __launch_bounds__(512) void expert_gemv_kernel(GemvKParams p) {
   constexpr int WN = GemvShape<OP>::WN, WK = GemvShape<OP>::WK;
   __shared__ GemvSmem<WN, WK, (OP == kOpGateUp) ? 2 : 1> sm;
   const GroupArgs& G = p.grp;
@@ -42,7 +42,8 @@ template <int FMT, int OP>
 hipError_t launch_t(const GemvKParams& p, hipStream_t s) {
   constexpr int RPB = gemv_rows_per_block<OP>();
   dim3 grid((p.w0.rows + RPB - 1) / RPB, p.grp.shared ? 1 : p.grp.max_groups);
-  return launch(expert_gemv_kernel<FMT, OP>, grid, dim3(256), 0, s, p);
+  constexpr int threads = kWave * GemvShape<OP>::WN * GemvShape<OP>::WK;
+  return launch(expert_gemv_kernel<FMT, OP>, grid, dim3(threads), 0, s, p);
 }
 
 template <int FMT>
