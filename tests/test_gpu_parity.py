@@ -361,3 +361,61 @@ def test_workspace_reuse_across_batch_sizes():
         ref = O.layer_forward(L, x_bits)
         assert np.array_equal(ids.cpu().numpy(), ref.routing.ids), T
         assert_close(O.bf16_value(bf16_bits(out)), ref.out, f"reuse T={T}")
+
+
+def _degenerate_layer(fmt):
+    """A small layer whose routed experts 0..4 (all tokens route to them: a
+    +20 router bias, k = 5) carry degenerate weights: a NaN block scale in
+    one down-projection row, a NaN element of an FP8 code, subnormal and zero
+    scales, maximum-magnitude codes, an all-zero expert, a zero tensor scale,
+    and a NaN block scale in the shared expert's down projection."""
+    import dataclasses
+    w = synth.scaled(W["tiny_nvfp4_t4"], name=f"degenerate_{fmt}", T=40, H=352, E=8, I=160,
+                     top_k=5, fmt=fmt, I_shared=96, shared_fmt=synth.FMT_FP8)
+    L = layer_for(w)
+
+    def clone(q):
+        return dataclasses.replace(q, codes=q.codes.copy(), scales=q.scales.copy(),
+                                   tensor_scale=None if q.tensor_scale is None else q.tensor_scale.copy())
+    gate, up, down, sd = clone(L.gate), clone(L.up), clone(L.down), clone(L.sh_down)
+    if fmt == synth.FMT_NVFP4:
+        down.scales[0, 5, 1] = 0x7F          # E4M3 NaN: column 5 of expert 0's output
+        up.codes[1] = 0x77                   # every code +6 ...
+        up.scales[1] = 0x7E                  # ... times the largest scale, 448
+        gate.scales[2] = 0x01                # smallest subnormal scale, 2^-9
+        down.scales[2, :, ::2] = 0x00        # zero scales in half the blocks
+        gate.codes[3] = 0
+        up.codes[3] = 0                      # an all-zero expert
+        gate.tensor_scale[4] = 0.0           # zero tensor scale
+    elif fmt == synth.FMT_MXFP4:
+        down.scales[0, 7, 0] = 0xFF          # E8M0 NaN
+        up.scales[1] = 0                     # 2^-127
+        gate.codes[2] = 0x77
+        gate.scales[2] = 127 + 8             # 6 * 2^8
+        gate.codes[3] = 0
+        up.codes[3] = 0
+    else:
+        down.codes[0, 9, 17] = 0x7F          # E4M3 NaN code
+        up.codes[1] = 0x7E                   # 448 everywhere ...
+        up.scales[1] = 4.0                   # ... times 4
+        gate.codes[2] = 0x01                 # smallest subnormal code
+        gate.codes[3] = 0
+        up.codes[3] = 0
+    sd.scales[0, 0, 0] = np.nan              # shared down: rows 0..127 NaN
+    bias = np.zeros(w.E, dtype=np.float32)
+    bias[:5] = 20.0
+    L2 = dataclasses.replace(L, gate=gate, up=up, down=down, sh_down=sd, router_bias=bias)
+    return w, L2
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_NVFP4, synth.FMT_MXFP4, synth.FMT_FP8])
+@pytest.mark.parametrize("T", [5, 12, 40])
+def test_degenerate_weights(fmt, T):
+    """NaN, subnormal, zero and extreme checkpoint values through the decode
+    (T <= 8), small-group (T <= 16) and grouped-GEMM paths: same NaN pattern
+    as the oracle, the finite outputs within tolerance."""
+    w, L = _degenerate_layer(fmt)
+    x_bits = synth.make_x(w)[:T]
+    say(f"[gpu] degenerate weights fmt={fmt} T={T}")
+    r = check_layer_against_oracle(L, x_bits, what=f"degenerate {fmt} T={T}")
+    assert np.isnan(r["out"]).any() and np.isfinite(r["out"]).any()
