@@ -18,13 +18,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= H) return;
+  // Issue the loads of 8 slots before summing them (one memory round trip
+  // per batch, not per slot); the sum stays in slot order.
+  constexpr int B = 8;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int pp = p2p[(size_t)t * k + j];
-    const float wj = w[(size_t)t * k + j];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(y + (size_t)pp * H + n);
+  for (int j0 = 0; j0 < k; j0 += B) {
+    f32x4 v[B];
+    float wj[B];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+    for (int b = 0; b < B; ++b) {
+      const int j = min(j0 + b, k - 1);  // in bounds; slots past k are not summed
+      const int pp = p2p[(size_t)t * k + j];
+      wj[b] = w[(size_t)t * k + j];
+      v[b] = *reinterpret_cast<const f32x4*>(y + (size_t)pp * H + n);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (j0 + b >= k) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj[b], v[b][q], acc[q]);
+    }
   }
   if (ys != nullptr) acc = acc + *reinterpret_cast<const f32x4*>(ys + (size_t)t * H + n);
   const uint2 o = make_uint2(f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16),

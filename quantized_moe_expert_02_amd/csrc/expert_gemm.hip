@@ -139,41 +139,62 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
 
   // ---- staging roles: thread -> (tile row, K half) ----
   const int srow = tid >> 1, shalf = tid & 1;
-  // activation row
-  const uint16_t* arow = nullptr;
+  // Activation row.  Rows past the group (and, defensively, rows whose index
+  // is out of range) read row m0 / row 0 instead of zeros: an MFMA output
+  // row depends on its own A row only, and padding rows are never stored,
+  // so every full K step loads unconditionally.
+  const uint16_t* arow;
+  bool arow_ok;
   {
     const int pr = m0 + srow;
-    if (pr < m1) {
-      int ir;
-      if (p.tiles == nullptr)
-        ir = pr;
-      else if (OP == kOpGateUp)
-        ir = p.perm_to_pair[pr] / p.topk;
-      else
-        ir = pr;
-      if ((unsigned)ir < (unsigned)p.in_rows) arow = p.in + (size_t)ir * K;
-    }
+    const bool in_group = pr < m1;
+    const int row = in_group ? pr : m0;  // m0 < m1: a valid row of the group
+    int ir = (p.tiles != nullptr && OP == kOpGateUp) ? p.perm_to_pair[row] / p.topk : row;
+    arow_ok = in_group && (unsigned)ir < (unsigned)p.in_rows;
+    if ((unsigned)ir >= (unsigned)p.in_rows) ir = 0;
+    arow = p.in + (size_t)ir * K;
   }
-  // weight row: gate/up tiles hold 64 gate rows then the matching 64 up rows
+  // Weight row: gate/up tiles hold 64 gate rows then the matching 64 up rows.
+  // Rows past N read row N-1 (their output columns are never stored).
   const WDesc& wq = (OP == kOpGateUp && srow >= BN / 2) ? p.w1 : p.w0;
-  const int wr = (OP == kOpGateUp) ? n0 + (srow & (BN / 2 - 1)) : n0 + srow;
-  const bool wvalid = wr < N;
+  const int wr0 = (OP == kOpGateUp) ? n0 + (srow & (BN / 2 - 1)) : n0 + srow;
+  const bool wvalid = wr0 < N;
+  const int wr = wvalid ? wr0 : N - 1;
   const int rb = row_bytes<FMT>(K);
-  const uint8_t* wrow = wvalid ? wq.codes + e * wq.stride_codes + (size_t)wr * rb : nullptr;
-  const uint8_t* wsrow = wvalid ? scale_row_ptr<FMT>(wq, e, wr) : nullptr;
+  const uint8_t* wrow = wq.codes + e * wq.stride_codes + (size_t)wr * rb;
+  const uint8_t* wsrow = scale_row_ptr<FMT>(wq, e, wr);
 
-  auto load_stage = [&](int k0, Stage<FMT>& st) {
+  // A full K step (k0 + BK <= K): no guards.
+  auto load_full = [&](int k0, Stage<FMT>& st) {
+    const int kb = k0 + 32 * shalf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(arow + kb + 8 * i);
+    if constexpr (FMT == FMT_FP8) {
+      st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb);
+      st.q[1] = *reinterpret_cast<const u32x4*>(wrow + kb + 16);
+      st.s = 0;
+    } else {
+      st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb / 2);
+      st.q[1] = u32x4{0, 0, 0, 0};
+      if constexpr (FMT == FMT_NVFP4)
+        st.s = *reinterpret_cast<const uint16_t*>(wsrow + kb / 16);
+      else
+        st.s = wsrow[kb / 32];
+    }
+  };
+  // The last, partial K step: zeros past K on both operands.
+  auto load_tail = [&](int k0, Stage<FMT>& st) {
     const int kb = k0 + 32 * shalf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = kb + 8 * i;
-      st.a[i] = (arow != nullptr && k < K) ? *reinterpret_cast<const u32x4*>(arow + k)
-                                           : u32x4{0, 0, 0, 0};
+      st.a[i] = (arow_ok && k < K) ? *reinterpret_cast<const u32x4*>(arow + k)
+                                   : u32x4{0, 0, 0, 0};
     }
     st.q[0] = u32x4{0, 0, 0, 0};
     st.q[1] = u32x4{0, 0, 0, 0};
     st.s = 0;
-    if (wrow != nullptr && kb < K) {
+    if (wvalid && kb < K) {
       if constexpr (FMT == FMT_FP8) {
         st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb);
         if (kb + 16 < K) st.q[1] = *reinterpret_cast<const u32x4*>(wrow + kb + 16);
@@ -185,6 +206,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
           st.s = wsrow[kb / 32];
       }
     }
+  };
+  auto load_stage = [&](int k0, Stage<FMT>& st) {
+    if (k0 + BK <= K)
+      load_full(k0, st);
+    else
+      load_tail(k0, st);
   };
   auto store_stage = [&](int buf, const Stage<FMT>& st) {
     uint16_t* ad = &sm.a[buf][srow][32 * shalf];
