@@ -235,10 +235,11 @@ __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs
 // row of length K, for the calling wavefront.  The weights are decoded in
 // registers as in gemv_tile; the input row is the MFMA's B operand column 0.
 // Result: lane 16q holds output rows n0 + 4q + (0..3) (lanes with lane % 16
-// != 0 hold zeros).  Loads of four 128-wide chunks are issued together.
+// != 0 hold zeros), times the NVFP4 tensor scale.  Loads of four 128-wide
+// chunks are issued together; the tensor scale is loaded with the first four.
 template <int FMT>
 __device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const uint16_t* hrow,
-                                            int K) {
+                                            int K, ScaleXchg& sx) {
   const int lane = __lane_id(), r = lane & 15, g = lane >> 4;
   const int row = n0 + r;
   const uint8_t* rp = w.codes + e * w.stride_codes + (size_t)row * row_bytes<FMT>(K);
@@ -247,16 +248,36 @@ __device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const
   const int nch = (K + 127) / 128;
   constexpr int D = 4;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ts = 1.0f;
+  const bool wide = (FMT != FMT_FP8) && w.wide;
   for (int cb = 0; cb < nch; cb += D) {
     ARaw<FMT> ar[D];
     u32x4 bx[D][4];
+    uint2 sw = make_uint2(0u, 0u);
+    if (FMT != FMT_FP8 && wide) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) ar[d] = load_a<FMT>(cb + d < nch ? rp : nullptr, sp, cb + d, g, K);
+      for (int d = 0; d < D; ++d)
+        ar[d] = load_a<FMT, false>(cb + d < nch ? rp : nullptr, nullptr, cb + d, g, K);
+      sw = load_scale_word<FMT>(sp, cb + g, nch);
+    } else {
+#pragma unroll
+      for (int d = 0; d < D; ++d) ar[d] = load_a<FMT>(cb + d < nch ? rp : nullptr, sp, cb + d, g, K);
+    }
+    if constexpr (FMT == FMT_NVFP4) {
+      if (cb == 0) ts = w.tscale[e];
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         bx[d][i] = load_b(cb + d < nch ? brow : nullptr, 128 * (cb + d) + 32 * g + 8 * i, K);
+    if constexpr (FMT != FMT_FP8) {
+      if (wide) {
+        const uint2 o = exchange_scales<FMT>(sw, sx, r, g);
+#pragma unroll
+        for (int d = 0; d < D; ++d) ar[d].s = scale_of_chunk<FMT>(o, d);
+      }
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (cb + d >= nch) break;
@@ -271,21 +292,23 @@ __device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const
         acc = t;
     }
   }
-  return acc;
+  return acc * ts;
 }
 
 // Down projection of every routed slot of a token and of the shared expert,
 // combined in the same kernel: block (t, 16-column tile of H) of one
-// wavefront per slot (at most 16; wavefront w takes slots w, w + 16, ...;
+// wavefront per slot (at most 12; wavefront w takes slots w, w + 12, ...;
 // slot k = the shared expert), each writes its 16
 // outputs y_j to LDS, then out[t] = bf16(sum_j w_j * y_j + y_shared) in slot
 // order.  No per-pair y goes through memory.
 constexpr int kDcCols = 16;
-constexpr int kDcMaxWaves = 16;  // one wavefront per slot up to 16 slots
+constexpr int kDcMaxWaves = 12;  // one wavefront per slot up to 12 slots (168 VGPRs each)
 
 template <int RFMT, int SFMT>
 __global__ __launch_bounds__(kDcMaxWaves * kWave) void decode_down_combine_kernel(DecodeArgs a) {
   __shared__ float yp[kMaxTopK + 1][kDcCols];
+  __shared__ float wp[kMaxTopK];
+  __shared__ ScaleXchg sxd[kDcMaxWaves];
   const int ntiles = a.H / kDcCols;
   const int t = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
   const int n0 = tile * kDcCols;
@@ -294,27 +317,26 @@ __global__ __launch_bounds__(kDcMaxWaves * kWave) void decode_down_combine_kerne
   const int nwaves = blockDim.x / kWave;
   for (int j = wave; j < nslots; j += nwaves) {
     f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+    float wj = 0.f;
     if (j < a.k) {
       const int p = t * a.k + j;
       const int e = a.ids[p];
-      if ((unsigned)e < (unsigned)a.E) {
-        y = gemv16_row<RFMT>(a.down, e, n0, a.h + (size_t)p * a.I, a.I);
-        if constexpr (RFMT == FMT_NVFP4) y = y * a.down.tscale[e];
-      }
+      wj = a.w[p];  // the combine weight, fetched with the expert id
+      if ((unsigned)e < (unsigned)a.E) y = gemv16_row<RFMT>(a.down, e, n0, a.h + (size_t)p * a.I, a.I, sxd[wave]);
     } else if constexpr (SFMT != 0) {
-      y = gemv16_row<SFMT>(a.sd, 0, n0, a.hs + (size_t)t * a.I_shared, a.I_shared);
-      if constexpr (SFMT == FMT_NVFP4) y = y * a.sd.tscale[0];
+      y = gemv16_row<SFMT>(a.sd, 0, n0, a.hs + (size_t)t * a.I_shared, a.I_shared, sxd[wave]);
     }
     if ((lane & 15) == 0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) yp[j][4 * (lane >> 4) + q] = y[q];
     }
+    if (lane == 0 && j < a.k) wp[j] = wj;
   }
   __syncthreads();
   if ((int)threadIdx.x < kDcCols) {
     const int c = threadIdx.x;
     float acc = 0.f;
-    for (int j = 0; j < a.k; ++j) acc = fmaf(a.w[t * a.k + j], yp[j][c], acc);
+    for (int j = 0; j < a.k; ++j) acc = fmaf(wp[j], yp[j][c], acc);
     if constexpr (SFMT != 0) acc = acc + yp[a.k][c];
     a.out[(size_t)t * a.H + n0 + c] = f32_to_bf16(acc);
   }

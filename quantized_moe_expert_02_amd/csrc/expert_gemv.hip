@@ -23,10 +23,12 @@ __global__ __launch_bounds__(512) void expert_gemv_kernel(GemvKParams p) {
     gr = GemvRows{0, 0, G.T, nullptr, nullptr};
   } else {
     const int u = blockIdx.y;
-    if (u >= *G.n_act) return;
+    // both loads issued before either is used (act holds max_groups >= gridDim.y entries)
+    const int na = *G.n_act;
+    gr.e = G.act[u];
+    if (u >= na) return;
     const int P = G.T * G.topk;
     gr.rows_in = gr.rows_out = nullptr;
-    gr.e = G.act[u];
     if ((unsigned)gr.e >= (unsigned)G.E) return;
     gr.p0 = G.offsets[gr.e];
     gr.nrows = G.offsets[gr.e + 1] - gr.p0;

@@ -59,7 +59,8 @@ __device__ __forceinline__ int row_bytes(int K) {
 }
 
 // Load the lane's part of chunk c for weight row `row` (nullptr = zero row).
-template <int FMT>
+// SC = false: FP4 codes only (the scales come from exchange_scales).
+template <int FMT, bool SC = true>
 __device__ __forceinline__ ARaw<FMT> load_a(const uint8_t* __restrict__ row,
                                             const uint8_t* __restrict__ srow, int c, int g, int K) {
   ARaw<FMT> a;
@@ -78,10 +79,12 @@ __device__ __forceinline__ ARaw<FMT> load_a(const uint8_t* __restrict__ row,
     a.s = 0;
     if (row != nullptr && k0 < K) {
       a.q = *reinterpret_cast<const u32x4*>(row + k0 / 2);
-      if constexpr (FMT == FMT_NVFP4)
-        a.s = *reinterpret_cast<const uint16_t*>(srow + k0 / 16);
-      else
-        a.s = srow[k0 / 32];
+      if constexpr (SC) {
+        if constexpr (FMT == FMT_NVFP4)
+          a.s = *reinterpret_cast<const uint16_t*>(srow + k0 / 16);
+        else
+          a.s = srow[k0 / 32];
+      }
     }
   }
   return a;
@@ -154,6 +157,68 @@ __device__ __forceinline__ const uint8_t* scale_row_ptr(const WDesc& w, int e, i
            (size_t)(n / 128) * ((w.cols + 127) / 128) * 4;
 }
 
+// FP4 block scales by whole chunks (WDesc::wide).  The lane (r, g) that
+// needs the two NVFP4 (one MXFP4) scale bytes of K piece 32g..32g+31 of four
+// chunks would otherwise issue four 2-byte loads that each touch 16 rows'
+// scale lines; instead it loads the whole scale word (8 E4M3 / 4 E8M0 bytes)
+// of one chunk of its row, and a wave-local LDS transpose hands every lane
+// the bytes of its own K piece of each chunk.
+struct alignas(8) ScaleXchg {
+  uint16_t v[16][4][4];  // [row][K piece][chunk of the batch]
+};
+
+template <int FMT>
+__device__ __forceinline__ uint2 load_scale_word(const uint8_t* __restrict__ srow, int c, int nch) {
+  uint2 w = make_uint2(0u, 0u);
+  if (srow != nullptr && c < nch) {
+    if constexpr (FMT == FMT_NVFP4)
+      w = *reinterpret_cast<const uint2*>(srow + 8 * c);
+    else
+      w.x = *reinterpret_cast<const uint32_t*>(srow + 4 * c);
+  }
+  return w;
+}
+
+// Lane (r, g) passes the scale word of chunk g of a four-chunk batch (row r)
+// and receives, for chunk d of the batch, the ARaw::s of its K piece g in
+// bits [16d, 16d + 16) (NVFP4) or [8d, 8d + 8) (MXFP4).  Wave-local: the
+// lanes r + 16g of one row are in one wavefront.
+template <int FMT>
+__device__ __forceinline__ uint2 exchange_scales(uint2 w, ScaleXchg& x, int r, int g) {
+  if constexpr (FMT == FMT_NVFP4) {
+    x.v[r][0][g] = static_cast<uint16_t>(w.x);
+    x.v[r][1][g] = static_cast<uint16_t>(w.x >> 16);
+    x.v[r][2][g] = static_cast<uint16_t>(w.y);
+    x.v[r][3][g] = static_cast<uint16_t>(w.y >> 16);
+  } else {
+    uint8_t* b = reinterpret_cast<uint8_t*>(&x.v[r][0][0]);  // [K piece][chunk] bytes
+#pragma unroll
+    for (int p = 0; p < 4; ++p) b[4 * p + g] = static_cast<uint8_t>(w.x >> (8 * p));
+  }
+  // LDS accesses of one wavefront complete in order; this only keeps the
+  // compiler from moving the reads above the writes of the other lanes.
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
+  uint2 o;
+  if constexpr (FMT == FMT_NVFP4) {
+    o = *reinterpret_cast<const uint2*>(&x.v[r][g][0]);
+  } else {
+    o.x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(&x.v[r][0][0]) + 4 * g);
+    o.y = 0u;
+  }
+  __asm__ volatile("" ::: "memory");
+  return o;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_of_chunk(uint2 o, int d) {
+  if constexpr (FMT == FMT_NVFP4)
+    return ((d < 2 ? o.x : o.y) >> (16 * (d & 1))) & 0xffffu;
+  else
+    return (o.x >> (8 * d)) & 0xffu;
+}
+
 // Where a group's rows come from and go to.
 struct GemvRows {
   int e;                // expert index within the projection
@@ -183,6 +248,7 @@ struct GemvIO {
 template <int WN, int WK, int NT>
 struct GemvSmem {
   f32x4 red[WN * WK][NT][64];
+  ScaleXchg sx[WN * WK][NT];
 };
 
 // One workgroup (64*WN*WK threads): output rows [tile*16*WN, +16*WN) of one
@@ -193,6 +259,7 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
                                           GemvSmem<WN, WK, (OP == kOpGateUp) ? 2 : 1>& sm) {
   constexpr int NT = (OP == kOpGateUp) ? 2 : 1;  // weight tiles per wave
   constexpr int D = 4;                            // chunks in flight per wave
+  static_assert(D == 4, "exchange_scales maps lane group g to chunk g of a batch");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wn = wave / WK, wk = wave % WK;
   const int e = gr.e, p0 = gr.p0, nrows = gr.nrows;
@@ -214,6 +281,12 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
     srow[q] = on ? scale_row_ptr<FMT>(*wd[q], e, nrow) : nullptr;
   }
   const int nch = (K + 127) / 128;
+  const bool wide = (FMT != FMT_FP8) && w0.wide && (NT == 1 || wd[NT - 1]->wide);
+  // NVFP4 per-expert tensor scales: loaded with the first weight batch (not
+  // in the epilogue, where the load would cost one more memory round trip).
+  float ts[NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) ts[q] = 1.0f;
 
   for (int pass = 0; pass < nrows; pass += 16) {
     const int grow = pass + r;
@@ -235,15 +308,36 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
       bool first = true;
       for (int cb = wk; cb < nch; cb += WK * D) {
         ARaw<FMT> ar[D][NT];
+        uint2 sw[NT];
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-          const int c = cb + d * WK;
+        for (int q = 0; q < NT; ++q) sw[q] = make_uint2(0u, 0u);
+        if (FMT != FMT_FP8 && wide) {
 #pragma unroll
-          for (int q = 0; q < NT; ++q)
-            ar[d][q] = load_a<FMT>(c < nch ? arow[q] : nullptr, srow[q], c, g, K);
+          for (int d = 0; d < D; ++d) {
+            const int c = cb + d * WK;
+#pragma unroll
+            for (int q = 0; q < NT; ++q)
+              ar[d][q] = load_a<FMT, false>(c < nch ? arow[q] : nullptr, nullptr, c, g, K);
+          }
+#pragma unroll
+          for (int q = 0; q < NT; ++q) sw[q] = load_scale_word<FMT>(srow[q], cb + g * WK, nch);
+        } else {
+#pragma unroll
+          for (int d = 0; d < D; ++d) {
+            const int c = cb + d * WK;
+#pragma unroll
+            for (int q = 0; q < NT; ++q)
+              ar[d][q] = load_a<FMT>(c < nch ? arow[q] : nullptr, srow[q], c, g, K);
+          }
         }
         if (first) {
           first = false;
+          if constexpr (FMT == FMT_NVFP4) {
+            if (pass == 0) {
+#pragma unroll
+              for (int q = 0; q < NT; ++q) ts[q] = wd[q]->tscale[e];
+            }
+          }
           if (row_ok) {
             int in_row;
             if (io.mode == kInShared)
@@ -264,6 +358,16 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
           const int kb = 128 * c + 32 * g;
 #pragma unroll
           for (int i = 0; i < 4; ++i) bx[d][i] = load_b(c < nch ? brow : nullptr, kb + 8 * i, K);
+        }
+        if constexpr (FMT != FMT_FP8) {
+          if (wide) {
+#pragma unroll
+            for (int q = 0; q < NT; ++q) {
+              const uint2 o = exchange_scales<FMT>(sw[q], sm.sx[wave][q], r, g);
+#pragma unroll
+              for (int d = 0; d < D; ++d) ar[d][q].s = scale_of_chunk<FMT>(o, d);
+            }
+          }
         }
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -307,9 +411,6 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
       const int nb = n0 + 4 * g;
       const int orow = (io.mode == kInShared) ? grow
                        : (io.mode == kInList) ? gr.rows_out[grow] : p0 + grow;
-      float ts[NT];
-#pragma unroll
-      for (int q = 0; q < NT; ++q) ts[q] = (FMT == FMT_NVFP4) ? wd[q]->tscale[e] : 1.0f;
       if constexpr (OP == kOpGateUp) {
         uint16_t h[4];
 #pragma unroll

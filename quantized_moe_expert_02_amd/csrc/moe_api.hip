@@ -74,6 +74,9 @@ WDesc wdesc(const moe_qweight& q) {
   w.stride_scales = q.expert_stride_scales;
   w.rows = q.rows;
   w.cols = q.cols;
+  const size_t word = (q.format == MOE_FMT_NVFP4) ? 8 : (q.format == MOE_FMT_MXFP4 ? 4 : 0);
+  w.wide = word != 0 && q.cols % 128 == 0 && aligned(q.scales, word) &&
+           (q.num_experts == 1 || q.expert_stride_scales % (int64_t)word == 0);
   return w;
 }
 

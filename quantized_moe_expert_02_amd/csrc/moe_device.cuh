@@ -29,6 +29,10 @@ struct WDesc {
   long long stride_codes;   // bytes between experts
   long long stride_scales;  // bytes between experts
   int rows, cols;
+  // FP4 only: cols % 128 == 0 and every scale row starts 8-byte (NVFP4) or
+  // 4-byte (MXFP4) aligned, so the block scales of a 128-wide K chunk of a
+  // row are one aligned word.
+  int wide;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
