@@ -18,6 +18,8 @@
 //   (bf16 products exact in fp32, fp32 accumulation);
 // * blocks are ordered so that every column tile of one row tile lands on the
 //   same XCD (its activation rows stay in that XCD's L2).
+#include <type_traits>
+
 #include "gemv_core.cuh"
 
 namespace moe {
@@ -108,7 +110,8 @@ __device__ __forceinline__ void decode32(const Stage<FMT>& st, uint32_t (&w)[16]
 }
 
 template <int FMT, int OP>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == FMT_FP8 ? 1 : 2))) void grouped_gemm_kernel(
+    GemmParams p) {
   __shared__ GemmSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-aware order: workgroup b runs on XCD b % 8.  Each XCD takes a
@@ -207,11 +210,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
       }
     }
   };
-  auto load_stage = [&](int k0, Stage<FMT>& st) {
-    if (k0 + BK <= K)
+  // FAST (see the main loop): every K step is full, no guard.
+  auto load_stage = [&](int k0, Stage<FMT>& st, auto fast_t) {
+    if constexpr (decltype(fast_t)::value) {
       load_full(k0, st);
-    else
-      load_tail(k0, st);
+    } else {
+      if (k0 + BK <= K)
+        load_full(k0, st);
+      else
+        load_tail(k0, st);
+    }
   };
   auto store_stage = [&](int buf, const Stage<FMT>& st) {
     uint16_t* ad = &sm.a[buf][srow][32 * shalf];
@@ -251,8 +259,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
   const int nk = (K + BK - 1) / BK;
 
   // MFMAs of step ks on LDS buffer buf, and (FP8) the 128-wide K block close.
-  auto compute_step = [&](int buf, int ks) {
-    if (vr > 0) {
+  // FAST: all four 16-row tiles of the wave hold group rows (no per-tile
+  // branches, so the compiler can interleave these MFMAs with the next
+  // step's decode).
+  auto compute_step = [&](int buf, int ks, auto fast_t) {
+    constexpr bool FAST = decltype(fast_t)::value;
+    if (FAST || vr > 0) {
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 32) {
         bf16x8 af[4], bfr[4];
@@ -262,11 +274,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
           bfr[c] = *reinterpret_cast<const bf16x8*>(&sm.b[buf][bcol[c] + (lane & 15)][ko]);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (r < vr)
+          if (FAST || r < vr)
             af[r] = *reinterpret_cast<const bf16x8*>(&sm.a[buf][64 * wm + 16 * r + (lane & 15)][ko]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (r >= vr) continue;
+          if (!FAST && r >= vr) continue;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             if constexpr (FMT == FMT_FP8)
@@ -307,29 +319,39 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
   // global loads of steps ks+1 and ks+2 are outstanding, so each load has two
   // compute steps to arrive.  The loop is unrolled by two so that the
   // stages keep static register names.
-  Stage<FMT> s0, s1;
-  load_stage(0, s0);
-  store_stage(0, s0);
-  if (nk > 1) load_stage(BK, s0);
-  if (nk > 2) load_stage(2 * BK, s1);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ks += 2) {
-    // step ks on buffer 0; s0 holds step ks+1, s1 holds step ks+2
-    compute_step(0, ks);
-    if (ks + 1 < nk) {
-      store_stage(1, s0);
-      if (ks + 3 < nk) load_stage((ks + 3) * BK, s0);
-    }
+  // The loop body exists twice: a fast version for the common case (full
+  // 128-row tile half for this wave, K a multiple of BK), with no branch
+  // between the MFMAs, and the general one.  Both barriers are block-wide,
+  // so every wavefront of the block takes its own version safely.
+  auto main_loop = [&](auto fast_t) {
+    Stage<FMT> s0, s1;
+    load_stage(0, s0, fast_t);
+    store_stage(0, s0);
+    if (nk > 1) load_stage(BK, s0, fast_t);
+    if (nk > 2) load_stage(2 * BK, s1, fast_t);
     __syncthreads();
-    if (ks + 1 >= nk) break;
-    // step ks+1 on buffer 1; s1 holds step ks+2, s0 holds step ks+3
-    compute_step(1, ks + 1);
-    if (ks + 2 < nk) {
-      store_stage(0, s1);
-      if (ks + 4 < nk) load_stage((ks + 4) * BK, s1);
+    for (int ks = 0; ks < nk; ks += 2) {
+      // step ks on buffer 0; s0 holds step ks+1, s1 holds step ks+2
+      compute_step(0, ks, fast_t);
+      if (ks + 1 < nk) {
+        store_stage(1, s0);
+        if (ks + 3 < nk) load_stage((ks + 3) * BK, s0, fast_t);
+      }
+      __syncthreads();
+      if (ks + 1 >= nk) break;
+      // step ks+1 on buffer 1; s1 holds step ks+2, s0 holds step ks+3
+      compute_step(1, ks + 1, fast_t);
+      if (ks + 2 < nk) {
+        store_stage(0, s1);
+        if (ks + 4 < nk) load_stage((ks + 4) * BK, s1, fast_t);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
+  };
+  if (vr == 4 && K % BK == 0)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
 
   // ---- epilogue: lane holds rows 4*(lane/16)+j of each 16-row tile, column lane%16 ----
   const float ts0 = (FMT == FMT_NVFP4) ? p.w0.tscale[e] : 1.0f;
