@@ -338,7 +338,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == FMT_
     if (nk > 1) load_stage(BK, s0, fast_t);
     if (nk > 2) load_stage(2 * BK, s1, fast_t);
     __syncthreads();
-    for (int ks = 0; ks < nk; ks += 2) {
+    int ks = 0;
+    if constexpr (decltype(fast_t)::value) {
+      // Steady state without conditions (steps ks+1 .. ks+4 exist): each
+      // half-step is one basic block, which the scheduler can interleave.
+      for (; ks + 4 < nk; ks += 2) {
+        compute_step(0, ks, fast_t);
+        store_stage(1, s0);
+        load_stage((ks + 3) * BK, s0, fast_t);
+        __syncthreads();
+        compute_step(1, ks + 1, fast_t);
+        store_stage(0, s1);
+        load_stage((ks + 4) * BK, s1, fast_t);
+        __syncthreads();
+      }
+    }
+    for (; ks < nk; ks += 2) {
       // step ks on buffer 0; s0 holds step ks+1, s1 holds step ks+2
       compute_step(0, ks, fast_t);
       if (ks + 1 < nk) {
