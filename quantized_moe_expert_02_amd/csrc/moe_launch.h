@@ -72,7 +72,7 @@ inline PermPlan perm_plan(int T, int k) {
   p.NB = (p.P + kPermChunk - 1) / kPermChunk;
   return p;
 }
-// ws: hist [NB][E] int32 (base offsets written back in place)
+// ws: hist [NB][E] int32 (each chunk's rank base within its expert, written in place)
 hipError_t launch_permute(const int* ids, int T, int k, int E, int* counts, int* offsets,
                           int* perm_to_pair, int* pair_to_perm, int* hist, int* act,
                           int* n_act, int tile_m, int* tiles, int* n_tiles, int max_tiles,

@@ -67,20 +67,28 @@ __global__ __launch_bounds__(1024) void scan_kernel(int NB, int E, int* __restri
   if (from_offsets) {
     if (e < E) c = offsets[e + 1] - offsets[e];
   } else if (e < E) {
-    for (int b = 0; b < NB; ++b) {
-      const int h = hist[(size_t)b * E + e];
-      hist[(size_t)b * E + e] = c;  // rank base of chunk b within expert e
-      c += h;
+    // hist[b][e] becomes the rank of chunk b's first pair within expert e.
+    // The loads of a batch are issued before its stores (the stores may alias
+    // them), so a batch costs one memory round trip, not one per chunk.
+    constexpr int kB = 16;
+    for (int b0 = 0; b0 < NB; b0 += kB) {
+      int h[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) h[j] = (b0 + j < NB) ? hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (b0 + j < NB) {
+          hist[(size_t)(b0 + j) * E + e] = c;
+          c += h[j];
+        }
+      }
     }
     counts[e] = c;
   }
   int total;
   const int off = block_exclusive_scan(e < E ? c : 0, tmp, total);
   if (!from_offsets) {
-    if (e < E) {
-      offsets[e] = off;
-      for (int b = 0; b < NB; ++b) hist[(size_t)b * E + e] += off;
-    }
+    if (e < E) offsets[e] = off;  // the scatter adds it to the chunk ranks
     if (e == 0) offsets[E] = total;
   }
   // active experts in increasing id order
@@ -101,12 +109,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(int NB, int E, int* __restri
 
 // One wave per chunk; the chunk's pairs are ranked 64 at a time in order.
 __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids, int P, int E,
-                                                     const int* __restrict__ base,
+                                                     const int* __restrict__ rank0,
+                                                     const int* __restrict__ offsets,
                                                      int* __restrict__ perm_to_pair,
                                                      int* __restrict__ pair_to_perm) {
   __shared__ int cnt[kMaxExperts];
   const int b = blockIdx.x, lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) cnt[e] = base[(size_t)b * E + e];
+  // position of this chunk's first pair of expert e in the permuted order
+  for (int e = lane; e < E; e += 64) cnt[e] = offsets[e] + rank0[(size_t)b * E + e];
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
@@ -148,8 +158,8 @@ hipError_t launch_permute(const int* ids, int T, int k, int E, int* counts, int*
   e = launch(scan_kernel, dim3(1), dim3(1024), 0, s, pp.NB, E, hist, counts, offsets, act, n_act,
              tile_m, reinterpret_cast<int2*>(tiles), n_tiles, max_tiles, 0);
   if (e != hipSuccess) return e;
-  return launch(scatter_kernel, dim3(pp.NB), dim3(64), 0, s, ids, pp.P, E, hist, perm_to_pair,
-                pair_to_perm);
+  return launch(scatter_kernel, dim3(pp.NB), dim3(64), 0, s, ids, pp.P, E, hist, offsets,
+                perm_to_pair, pair_to_perm);
 }
 
 hipError_t launch_groups_from_offsets(const int* offsets, int E, int* act, int* n_act, int tile_m,
