@@ -115,7 +115,7 @@ __device__ __forceinline__ void decode32(const Stage<FMT>& st, uint32_t (&w)[16]
 }
 
 template <int FMT, int OP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == FMT_FP8 ? 1 : 2))) void grouped_gemm_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_kernel(
     GemmParams p) {
   __shared__ GemmSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
