@@ -115,9 +115,11 @@ struct RouterMfmaArgs {
   int n_mt, n_nt;
 };
 
+// One LDS stage (50 KB): two workgroups fit on a CU, so a 512-tile grid runs
+// in one round; the next step waits in registers while this one is read.
 struct RouterSmem {
-  uint16_t a[2][RBM][RLDS];
-  uint16_t b[2][3][RBN][RLDS];
+  uint16_t a[RBM][RLDS];
+  uint16_t b[3][RBN][RLDS];
   float wn[RBN];
 };
 
@@ -170,10 +172,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
                   : u32x4{0, 0, 0, 0};
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sm.a[buf][srow][8 * (2 * i + shalf)]) = ra[i];
+      *reinterpret_cast<u32x4*>(&sm.a[srow][8 * (2 * i + shalf)]) = ra[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float lo = __uint_as_float(ra[i][j] << 16), hi = __uint_as_float(ra[i][j] & 0xffff0000u);
@@ -185,8 +187,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
     for (int i = 0; i < 6; ++i) {
       const int c = tid + 256 * i;
       const int row = c >> 3, part = c & 7;  // K piece (half part / 4, index part % 4)
-      *reinterpret_cast<u32x4*>(&sm.b[buf][row / RBN][row % RBN][8 * (2 * (part & 3) + (part >> 2))]) =
-          rb[i];
+      *reinterpret_cast<u32x4*>(&sm.b[row / RBN][row % RBN][8 * (2 * (part & 3) + (part >> 2))]) = rb[i];
     }
   };
 
@@ -202,10 +203,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
 
   const int nk = (H + RBK - 1) / RBK;
   load(0);
-  store(0);
+  store();
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
     const bool more = ks + 1 < nk;
     if (more) load((ks + 1) * RBK);
     f32x4 cacc[4][2];
@@ -219,13 +219,13 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
       bf16x8 af[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        af[r] = *reinterpret_cast<const bf16x8*>(&sm.a[buf][64 * wm + 16 * r + (lane & 15)][ko]);
+        af[r] = *reinterpret_cast<const bf16x8*>(&sm.a[64 * wm + 16 * r + (lane & 15)][ko]);
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
         bf16x8 bfr[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          bfr[c] = *reinterpret_cast<const bf16x8*>(&sm.b[buf][s][32 * wn + 16 * c + (lane & 15)][ko]);
+          bfr[c] = *reinterpret_cast<const bf16x8*>(&sm.b[s][32 * wn + 16 * c + (lane & 15)][ko]);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -239,7 +239,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) dacc[r][c][j] += static_cast<double>(cacc[r][c][j]);
-    if (more) store(buf ^ 1);
+    __syncthreads();  // every wavefront has read this step
+    if (more) store();
     __syncthreads();
   }
 
