@@ -167,20 +167,36 @@ __global__ __launch_bounds__(kWave * kWaveTopkTokens) void topk_wave_kernel(Topk
   const int E = a.E;
   double* v = vals[wave];
   float m = 0.f;
-  if (a.mode == 0) {
-    for (int e = lane; e < E; e += kWave) v[e] = static_cast<double>(a.part[(size_t)t * E + e]);
-  } else {
-    for (int e = lane; e < E; e += kWave) {
-      double l = static_cast<double>(a.part[(size_t)t * E + e]);  // one slice
-      if (a.bias != nullptr) {
-        l += static_cast<double>(a.bias[e]);
-        m = fmaxf(m, fabsf(a.bias[e]));
-      }
-      v[e] = l;
-      if (a.logits_out != nullptr) a.logits_out[(size_t)t * E + e] = static_cast<float>(l);
-    }
-    for (int c = lane; c < a.CS; c += kWave) m = fmaxf(m, a.amax[(size_t)c * a.T + t]);
+  // All of a lane's loads (logits, offsets, bounds) are issued before any of
+  // the stores below, which the compiler must otherwise assume may alias
+  // them (one memory round trip per value).
+  const int nper = (E + kWave - 1) / kWave;
+  float pv[kMaxPerLane], bv[kMaxPerLane];
+  const bool has_bias = a.mode != 0 && a.bias != nullptr;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + kWave * i;
+    const bool on = i < nper && e < E;
+    pv[i] = on ? a.part[(size_t)t * E + e] : 0.f;
+    bv[i] = (on && has_bias) ? a.bias[e] : 0.f;
   }
+  float am = 0.f;
+  if (a.mode != 0) {
+    for (int c = lane; c < a.CS; c += kWave) am = fmaxf(am, a.amax[(size_t)c * a.T + t]);
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + kWave * i;
+    if (i >= nper || e >= E) continue;
+    double l = static_cast<double>(pv[i]);
+    if (has_bias) {  // mode 1: one slice plus the expert offset
+      l += static_cast<double>(bv[i]);
+      m = fmaxf(m, fabsf(bv[i]));
+    }
+    v[e] = l;
+    if (a.mode != 0 && a.logits_out != nullptr) a.logits_out[(size_t)t * E + e] = static_cast<float>(l);
+  }
+  m = fmaxf(m, am);
   m = wave_max_f(m);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();

@@ -97,6 +97,77 @@ __device__ inline double dd_logit(const uint16_t* __restrict__ xrow, const float
   return (s - s == 0.0) ? s + c : s;
 }
 
+// dd_logit for up to four experts of one token at once, with contiguous
+// expert rows (w + e * se, K stride 1).  Each expert's sum takes the same
+// terms in the same order as dd_logit (identical results); the x loads are
+// shared and the four rows' loads are in flight together, so a batch costs
+// about one memory round trip.  e[q] < 0: slot unused (out[q] = 0).
+__device__ inline void dd_logits4(const uint16_t* __restrict__ xrow, const float* __restrict__ w,
+                                  size_t se, int H, const int (&e)[4], const float* bias,
+                                  double (&out)[4]) {
+  constexpr int D = 2;  // with dd_logit's D = 4 the per-lane term order is the same
+  const int lane = __lane_id();
+  double s[4], c[4];
+  const float* we[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    s[q] = 0.0;
+    c[q] = 0.0;
+    we[q] = w + (size_t)(e[q] >= 0 ? e[q] : 0) * se;
+  }
+  for (int hb = 0; hb < H; hb += 8 * kWave * D) {
+    u32x4 xv[D];
+    f32x4 w0[4][D], w1[4][D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int h = hb + 8 * (lane + kWave * d);
+      const int hh = h < H ? h : 0;
+      xv[d] = *reinterpret_cast<const u32x4*>(xrow + hh);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w0[q][d] = *reinterpret_cast<const f32x4*>(we[q] + hh);
+        w1[q][d] = *reinterpret_cast<const f32x4*>(we[q] + hh + 4);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (hb + 8 * (lane + kWave * d) >= H) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float xl = __uint_as_float(xv[d][j] << 16);
+        const float xh = __uint_as_float(xv[d][j] & 0xffff0000u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (e[q] < 0) continue;
+          const float wl = (j < 2) ? w0[q][d][2 * j] : w1[q][d][2 * j - 4];
+          const float wh = (j < 2) ? w0[q][d][2 * j + 1] : w1[q][d][2 * j - 3];
+          dd_add(s[q], c[q], static_cast<double>(xl) * static_cast<double>(wl));
+          dd_add(s[q], c[q], static_cast<double>(xh) * static_cast<double>(wh));
+        }
+      }
+    }
+  }
+  for (int m = 1; m < kWave; m <<= 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double os = __shfl_xor(s[q], m, kWave);
+      const double oc = __shfl_xor(c[q], m, kWave);
+      double err;
+      two_sum(s[q], os, s[q], err);
+      c[q] = (c[q] + oc) + err;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (e[q] < 0) {
+      out[q] = 0.0;
+      continue;
+    }
+    if (bias != nullptr) dd_add(s[q], c[q], static_cast<double>(bias[e[q]]));
+    out[q] = (s[q] - s[q] == 0.0) ? s[q] + c[q] : s[q];
+  }
+}
+
 struct TopkToken {
   double* vals;        // LDS, [E] logits of this token (may be overwritten)
   int E, k, renorm;
@@ -433,38 +504,39 @@ __device__ __forceinline__ void wave_lds_sync() {
 // The `rounds`-th largest fp32-rounded key is found by bisection; the
 // candidates at or above it (at most 64, else the round-by-round selection
 // takes over) are ranked exactly on order_key.
-__device__ inline int wave_rank_select(const double* vals, int E, uint32_t excl, int rounds,
-                                       WaveTopkScratch& sc, double& top_v, int& top_i, int& top_c) {
+// NP: keys per lane, a power of two >= ceil(E / 64).  Keys past E are 0 and
+// never reach the threshold (>= 1), so every loop below is fully unrolled
+// with no per-element branch.
+template <int NP>
+__device__ inline int wave_rank_select_np(const double* vals, int E, uint32_t excl, int rounds,
+                                          WaveTopkScratch& sc, double& top_v, int& top_i,
+                                          int& top_c) {
   const int lane = __lane_id();
-  const int nper = (E + kWave - 1) / kWave;
-  uint32_t c[kMaxPerLane];
+  uint32_t c[NP];
   int elig = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int e = lane + kWave * i;
-    c[i] = (i < nper && e < E) ? coarse_key(vals[e], (excl >> i) & 1u) : 0u;
-    if (i < nper) elig += __popcll(__ballot(c[i] != 0u));
+    c[i] = (e < E) ? coarse_key(vals[e], (excl >> i) & 1u) : 0u;
+    elig += __popcll(__ballot(c[i] != 0u));
   }
   uint32_t t = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = t | (1u << bit);
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (i < nper) cnt += __popcll(__ballot(c[i] >= cand));
+    for (int i = 0; i < NP; ++i) cnt += __popcll(__ballot(c[i] >= cand));
     if (cnt >= rounds) t = cand;
   }
   if (t == 0u) t = 1u;  // fewer than `rounds` eligible: every eligible logit
   int nc = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i)
-    if (i < nper) nc += __popcll(__ballot(c[i] >= t));
+  for (int i = 0; i < NP; ++i) nc += __popcll(__ballot(c[i] >= t));
   if (nc > kWave) return wave_select(vals, E, excl, rounds, top_v, top_i, top_c);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   int base = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    if (i >= nper) break;
+  for (int i = 0; i < NP; ++i) {
     const bool q = c[i] >= t;
     const uint64_t b = __ballot(q);
     if (q) {
@@ -496,6 +568,16 @@ __device__ inline int wave_rank_select(const double* vals, int E, uint32_t excl,
   }
   wave_lds_sync();
   return got;
+}
+
+__device__ inline int wave_rank_select(const double* vals, int E, uint32_t excl, int rounds,
+                                       WaveTopkScratch& sc, double& top_v, int& top_i, int& top_c) {
+  const int nper = (E + kWave - 1) / kWave;
+  if (nper <= 1) return wave_rank_select_np<1>(vals, E, excl, rounds, sc, top_v, top_i, top_c);
+  if (nper <= 2) return wave_rank_select_np<2>(vals, E, excl, rounds, sc, top_v, top_i, top_c);
+  if (nper <= 4) return wave_rank_select_np<4>(vals, E, excl, rounds, sc, top_v, top_i, top_c);
+  if (nper <= 8) return wave_rank_select_np<8>(vals, E, excl, rounds, sc, top_v, top_i, top_c);
+  return wave_rank_select_np<kMaxPerLane>(vals, E, excl, rounds, sc, top_v, top_i, top_c);
 }
 
 // Select, certify (optionally recompute), and write ids and weights.
@@ -540,6 +622,21 @@ __device__ inline void wave_topk(const TopkToken& a) {
       wave_lds_sync();
       if (lane < k && lane < got && (close_r || close_prev)) sc.mark[top_i] = 1;
       wave_lds_sync();
+      // Contiguous expert rows: candidates go four at a time (dd_logits4).
+      int eb[4] = {-1, -1, -1, -1};
+      int nb = 0;
+      auto flush = [&]() {
+        double v4[4];
+        dd_logits4(a.xrow, a.wr, a.wr_se, a.H, eb, a.bias, v4);
+        if (lane == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (eb[q] >= 0) a.vals[eb[q]] = v4[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) eb[q] = -1;
+        nb = 0;
+      };
       for (int i = 0; i < nper; ++i) {
         const int e = lane + kWave * i;
         const double v = (e < E) ? a.vals[e] : 0.0;
@@ -549,10 +646,20 @@ __device__ inline void wave_topk(const TopkToken& a) {
         while (mask) {
           const int l = __builtin_ctzll(mask);
           mask &= mask - 1;
-          const double val = dd_logit(a.xrow, a.wr, a.wr_sh, a.wr_se, a.H, l + kWave * i, a.bias);
-          if (lane == 0) a.vals[l + kWave * i] = val;
+          if (a.wr_sh == 1) {
+            const int ec = l + kWave * i;
+            if (nb == 0) eb[0] = ec;
+            else if (nb == 1) eb[1] = ec;
+            else if (nb == 2) eb[2] = ec;
+            else eb[3] = ec;
+            if (++nb == 4) flush();
+          } else {
+            const double val = dd_logit(a.xrow, a.wr, a.wr_sh, a.wr_se, a.H, l + kWave * i, a.bias);
+            if (lane == 0) a.vals[l + kWave * i] = val;
+          }
         }
       }
+      if (nb > 0) flush();
       wave_lds_sync();
       got = wave_rank_select(a.vals, E, excl, k, *a.sc, top_v, top_i, top_c);
     }
