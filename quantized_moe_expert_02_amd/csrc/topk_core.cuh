@@ -520,15 +520,16 @@ __device__ inline int wave_rank_select_np(const double* vals, int E, uint32_t ex
     c[i] = (e < E) ? coarse_key(vals[e], (excl >> i) & 1u) : 0u;
     elig += __popcll(__ballot(c[i] != 0u));
   }
-  uint32_t t = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = t | (1u << bit);
-    int cnt = 0;
+  // Threshold: the `rounds`-th largest of the 64 lane maxima.  Those are
+  // `rounds` distinct keys, so the `rounds`-th largest key overall is at least
+  // this value, and every member of the first `rounds` (exact order; coarse
+  // keys are monotone in it) has a key at or above it.  One key per lane in
+  // the bisection instead of NP.
+  uint32_t lmax[1] = {0u};
 #pragma unroll
-    for (int i = 0; i < NP; ++i) cnt += __popcll(__ballot(c[i] >= cand));
-    if (cnt >= rounds) t = cand;
-  }
-  if (t == 0u) t = 1u;  // fewer than `rounds` eligible: every eligible logit
+  for (int i = 0; i < NP; ++i) lmax[0] = c[i] > lmax[0] ? c[i] : lmax[0];
+  uint32_t t = wave_kth_key<1>(lmax, rounds);
+  if (t == 0u) t = 1u;  // fewer than `rounds` lanes hold an eligible logit: all eligible
   int nc = 0;
 #pragma unroll
   for (int i = 0; i < NP; ++i) nc += __popcll(__ballot(c[i] >= t));
