@@ -158,25 +158,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 // leave early.
 constexpr int kWaveTopkTokens = 4;
 
+// NP: logits per lane, a power of two >= ceil(E / 64).  LDS (sized at launch
+// by topk_wave_lds): per wavefront 64 * NP float64 logits, then the
+// wavefronts' scratch; every slot a loop below can touch is inside it.
+template <int NP>
 __global__ __launch_bounds__(kWave * kWaveTopkTokens) void topk_wave_kernel(TopkArgs a) {
-  __shared__ double vals[kWaveTopkTokens][kMaxExperts];
-  __shared__ WaveTopkScratch scratch[kWaveTopkTokens];
+  extern __shared__ __align__(16) unsigned char topk_lds[];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  double* const vals = reinterpret_cast<double*>(topk_lds);
+  WaveTopkScratch* const scratch = reinterpret_cast<WaveTopkScratch*>(
+      topk_lds + sizeof(double) * kWaveTopkTokens * kWave * NP);
   const int t = blockIdx.x * kWaveTopkTokens + wave;
   if (t >= a.T) return;
   const int E = a.E;
-  double* v = vals[wave];
+  double* v = vals + (size_t)wave * kWave * NP;
   float m = 0.f;
   // All of a lane's loads (logits, offsets, bounds) are issued before any of
   // the stores below, which the compiler must otherwise assume may alias
   // them (one memory round trip per value).
-  const int nper = (E + kWave - 1) / kWave;
-  float pv[kMaxPerLane], bv[kMaxPerLane];
+  float pv[NP], bv[NP];
   const bool has_bias = a.mode != 0 && a.bias != nullptr;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int e = lane + kWave * i;
-    const bool on = i < nper && e < E;
+    const bool on = e < E;
     pv[i] = on ? a.part[(size_t)t * E + e] : 0.f;
     bv[i] = (on && has_bias) ? a.bias[e] : 0.f;
   }
@@ -185,9 +190,9 @@ __global__ __launch_bounds__(kWave * kWaveTopkTokens) void topk_wave_kernel(Topk
     for (int c = lane; c < a.CS; c += kWave) am = fmaxf(am, a.amax[(size_t)c * a.T + t]);
   }
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int e = lane + kWave * i;
-    if (i >= nper || e >= E) continue;
+    if (e >= E) continue;
     double l = static_cast<double>(pv[i]);
     if (has_bias) {  // mode 1: one slice plus the expert offset
       l += static_cast<double>(bv[i]);
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kWave * kWaveTopkTokens) void topk_wave_kernel(Topk
   tk.ids = a.ids + (size_t)t * a.k;
   tk.w = a.w + (size_t)t * a.k;
   tk.recomputed = a.recomputed ? a.recomputed + t : nullptr;
-  tk.sc = &scratch[wave];
+  tk.sc = scratch + wave;
   wave_topk(tk);
 }
 
@@ -228,11 +233,23 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H
   return launch(router_logits_kernel, grid, dim3(256), 0, s, x, wr, T, H, E, rp.RH, part, amax);
 }
 
+template <int NP>
+hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
+  const size_t lds = kWaveTopkTokens * (sizeof(double) * kWave * NP + sizeof(WaveTopkScratch));
+  return launch(topk_wave_kernel<NP>, dim3((a.T + kWaveTopkTokens - 1) / kWaveTopkTokens),
+                dim3(kWave * kWaveTopkTokens), lds, s, a);
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.wave) {
     if (a.mode == 1 && (a.RS != 1 || a.wrt == nullptr)) return hipErrorInvalidValue;
-    return launch(topk_wave_kernel, dim3((a.T + kWaveTopkTokens - 1) / kWaveTopkTokens),
-                  dim3(kWave * kWaveTopkTokens), 0, s, a);
+    if (a.E < 1 || a.E > kMaxExperts) return hipErrorInvalidValue;
+    const int nper = (a.E + kWave - 1) / kWave;
+    if (nper <= 1) return launch_topk_wave<1>(a, s);
+    if (nper <= 2) return launch_topk_wave<2>(a, s);
+    if (nper <= 4) return launch_topk_wave<4>(a, s);
+    if (nper <= 8) return launch_topk_wave<8>(a, s);
+    return launch_topk_wave<kMaxPerLane>(a, s);
   }
   return launch(topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
 }
