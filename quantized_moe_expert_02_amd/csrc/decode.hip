@@ -237,9 +237,9 @@ __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs
 // Result: lane 16q holds output rows n0 + 4q + (0..3) (lanes with lane % 16
 // != 0 hold zeros), times the NVFP4 tensor scale.  Loads of four 128-wide
 // chunks are issued together; the tensor scale is loaded with the first four.
-template <int FMT>
-__device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const uint16_t* hrow,
-                                            int K, ScaleXchg& sx) {
+template <int FMT, bool WIDE>
+__device__ __forceinline__ f32x4 gemv16_row_impl(const WDesc& w, int e, int n0, const uint16_t* hrow,
+                                                 int K, ScaleXchg& sx) {
   const int lane = __lane_id(), r = lane & 15, g = lane >> 4;
   const int row = n0 + r;
   const uint8_t* rp = w.codes + e * w.stride_codes + (size_t)row * row_bytes<FMT>(K);
@@ -249,12 +249,12 @@ __device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const
   constexpr int D = 4;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float ts = 1.0f;
-  const bool wide = (FMT != FMT_FP8) && w.wide;
+  constexpr bool wide = WIDE && FMT != FMT_FP8;
   for (int cb = 0; cb < nch; cb += D) {
     ARaw<FMT> ar[D];
     u32x4 bx[D][4];
     uint2 sw = make_uint2(0u, 0u);
-    if (FMT != FMT_FP8 && wide) {
+    if constexpr (wide) {
 #pragma unroll
       for (int d = 0; d < D; ++d)
         ar[d] = load_a<FMT, false>(cb + d < nch ? rp : nullptr, nullptr, cb + d, g, K);
@@ -271,12 +271,10 @@ __device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         bx[d][i] = load_b(cb + d < nch ? brow : nullptr, 128 * (cb + d) + 32 * g + 8 * i, K);
-    if constexpr (FMT != FMT_FP8) {
-      if (wide) {
-        const uint2 o = exchange_scales<FMT>(sw, sx, r, g);
+    if constexpr (wide) {
+      const uint2 o = exchange_scales<FMT>(sw, sx, r, g);
 #pragma unroll
-        for (int d = 0; d < D; ++d) ar[d].s = scale_of_chunk<FMT>(o, d);
-      }
+      for (int d = 0; d < D; ++d) ar[d].s = scale_of_chunk<FMT>(o, d);
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -293,6 +291,15 @@ __device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const
     }
   }
   return acc * ts;
+}
+
+template <int FMT>
+__device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const uint16_t* hrow,
+                                            int K, ScaleXchg& sx) {
+  if constexpr (FMT != FMT_FP8) {
+    if (w.wide) return gemv16_row_impl<FMT, true>(w, e, n0, hrow, K, sx);
+  }
+  return gemv16_row_impl<FMT, false>(w, e, n0, hrow, K, sx);
 }
 
 // Down projection of every routed slot of a token and of the shared expert,

@@ -76,7 +76,10 @@ __device__ __forceinline__ ARaw<FMT> load_a(const uint8_t* __restrict__ row,
     }
   } else {
     a.q = u32x4{0, 0, 0, 0};
-    a.s = 0;
+    // SC = false: s is written by the caller (exchange_scales); leaving it
+    // unwritten here keeps the compiler from waiting on every load in flight
+    // before the zeroing (the registers double as the 2-byte loads' targets).
+    if constexpr (SC) a.s = 0;
     if (row != nullptr && k0 < K) {
       a.q = *reinterpret_cast<const u32x4*>(row + k0 / 2);
       if constexpr (SC) {
@@ -253,10 +256,12 @@ struct GemvSmem {
 
 // One workgroup (64*WN*WK threads): output rows [tile*16*WN, +16*WN) of one
 // expert projection for every row of the group.  `sm` must be block-shared.
-template <int FMT, int OP, int WN, int WK>
-__device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, const GemvIO& io,
-                                          const GemvRows& gr, int tile,
-                                          GemvSmem<WN, WK, (OP == kOpGateUp) ? 2 : 1>& sm) {
+// WIDE: FP4 scales by whole chunks (exchange_scales); a separate copy of the
+// body, so that neither copy carries the other's registers or load waits.
+template <int FMT, int OP, int WN, int WK, bool WIDE>
+__device__ __forceinline__ void gemv_tile_impl(const WDesc& w0, const WDesc& w1, const GemvIO& io,
+                                               const GemvRows& gr, int tile,
+                                               GemvSmem<WN, WK, (OP == kOpGateUp) ? 2 : 1>& sm) {
   constexpr int NT = (OP == kOpGateUp) ? 2 : 1;  // weight tiles per wave
   constexpr int D = 4;                            // chunks in flight per wave
   static_assert(D == 4, "exchange_scales maps lane group g to chunk g of a batch");
@@ -281,7 +286,7 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
     srow[q] = on ? scale_row_ptr<FMT>(*wd[q], e, nrow) : nullptr;
   }
   const int nch = (K + 127) / 128;
-  const bool wide = (FMT != FMT_FP8) && w0.wide && (NT == 1 || wd[NT - 1]->wide);
+  constexpr bool wide = WIDE && FMT != FMT_FP8;
   // NVFP4 per-expert tensor scales: loaded with the first weight batch (not
   // in the epilogue, where the load would cost one more memory round trip).
   float ts[NT];
@@ -311,7 +316,7 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
         uint2 sw[NT];
 #pragma unroll
         for (int q = 0; q < NT; ++q) sw[q] = make_uint2(0u, 0u);
-        if (FMT != FMT_FP8 && wide) {
+        if constexpr (wide) {
 #pragma unroll
           for (int d = 0; d < D; ++d) {
             const int c = cb + d * WK;
@@ -359,14 +364,12 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
 #pragma unroll
           for (int i = 0; i < 4; ++i) bx[d][i] = load_b(c < nch ? brow : nullptr, kb + 8 * i, K);
         }
-        if constexpr (FMT != FMT_FP8) {
-          if (wide) {
+        if constexpr (wide) {
 #pragma unroll
-            for (int q = 0; q < NT; ++q) {
-              const uint2 o = exchange_scales<FMT>(sw[q], sm.sx[wave][q], r, g);
+          for (int q = 0; q < NT; ++q) {
+            const uint2 o = exchange_scales<FMT>(sw[q], sm.sx[wave][q], r, g);
 #pragma unroll
-              for (int d = 0; d < D; ++d) ar[d][q].s = scale_of_chunk<FMT>(o, d);
-            }
+            for (int d = 0; d < D; ++d) ar[d][q].s = scale_of_chunk<FMT>(o, d);
           }
         }
 #pragma unroll
@@ -439,6 +442,19 @@ __device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, cons
       }
     }
   }
+}
+
+template <int FMT, int OP, int WN, int WK>
+__device__ __forceinline__ void gemv_tile(const WDesc& w0, const WDesc& w1, const GemvIO& io,
+                                          const GemvRows& gr, int tile,
+                                          GemvSmem<WN, WK, (OP == kOpGateUp) ? 2 : 1>& sm) {
+  if constexpr (FMT != FMT_FP8) {
+    if (w0.wide && (OP != kOpGateUp || w1.wide)) {
+      gemv_tile_impl<FMT, OP, WN, WK, true>(w0, w1, io, gr, tile, sm);
+      return;
+    }
+  }
+  gemv_tile_impl<FMT, OP, WN, WK, false>(w0, w1, io, gr, tile, sm);
 }
 
 // Tile shapes: gate/up splits K across 4 waves of one 16-row tile; down
