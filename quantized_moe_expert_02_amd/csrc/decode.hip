@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
 }
 
 __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a) {
-  __shared__ BlockTopkSmem sm;
+  __shared__ double v[kMaxExperts];
+  __shared__ WaveTopkScratch wsc;
   __shared__ float amax_w[kTopkThreads / kWave];
   const int t = blockIdx.x, T = a.T, E = a.E;
   float amax = 0.f;
@@ -128,29 +129,37 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a)
       l += static_cast<double>(b);
       av += fabsf(b);
     }
-    sm.v[e] = l;
+    v[e] = l;
     if (a.logits_out != nullptr) a.logits_out[(size_t)t * E + e] = static_cast<float>(l);
     amax = fmaxf(amax, av);
   }
   amax = wave_max_f(amax);
   if ((threadIdx.x & (kWave - 1)) == 0) amax_w[threadIdx.x / kWave] = amax;
   __syncthreads();
+  // The selection runs on one wavefront (no block barriers): threshold from
+  // the lane maxima, exact ranking of the candidates, certification.
+  if (threadIdx.x >= kWave) return;
   float am = 0.f;
   for (int i = 0; i < (int)(blockDim.x / kWave); ++i) am = fmaxf(am, amax_w[i]);
-  BlockTopkArgs ta;
-  ta.E = E;
-  ta.k = a.k;
-  ta.renorm = a.renorm;
+  TopkToken tk;
+  tk.vals = v;
+  tk.E = E;
+  tk.k = a.k;
+  tk.renorm = a.renorm;
   // fast-logit error < 2^-23 * sum|x||w| (covers the fp32 slice roundings)
-  ta.bound = static_cast<double>(am) * 0x1p-23;
-  ta.certify = true;
-  ta.xrow = a.x + (size_t)t * a.H;
-  ta.wr = a.wr;
-  ta.bias = a.bias;
-  ta.H = a.H;
-  ta.ids = a.ids + (size_t)t * a.k;
-  ta.w = a.w + (size_t)t * a.k;
-  block_topk(sm, ta);
+  tk.bound = static_cast<double>(am) * 0x1p-23;
+  tk.certify = true;
+  tk.xrow = a.x + (size_t)t * a.H;
+  tk.wr = a.wr;  // [H][E]
+  tk.wr_sh = (size_t)E;
+  tk.wr_se = 1;
+  tk.bias = a.bias;
+  tk.H = a.H;
+  tk.ids = a.ids + (size_t)t * a.k;
+  tk.w = a.w + (size_t)t * a.k;
+  tk.recomputed = nullptr;
+  tk.sc = &wsc;
+  wave_topk(tk);
 }
 
 // Expert group of pair slot q: the expert e = ids[q] and all (token, slot)
