@@ -33,6 +33,13 @@ SMALL = {
     # above the fused decode size, at most one GEMV pass per group
     "nvfp4_t12": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t12", T=12, H=288, E=8, I=96,
                               top_k=3, I_shared=64, shared_fmt=synth.FMT_MXFP4),
+    # K a multiple of 128 (FP4 block scales read by whole chunk): 8 and 3
+    # chunks (the last batch of the down projection is partial)
+    "nvfp4_aligned": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_aligned", T=6, H=1024, E=12,
+                                  I=384, top_k=3, I_shared=128, shared_fmt=synth.FMT_NVFP4),
+    "mxfp4_aligned": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp4_aligned", T=11, H=768, E=10,
+                                  I=256, top_k=2, fmt=synth.FMT_MXFP4, I_shared=256,
+                                  shared_fmt=synth.FMT_MXFP4, zipf_s=1.1),
 }
 
 
@@ -272,7 +279,8 @@ def test_permute_bit_exact(T, k, E, skew):
     assert np.array_equal(q2.cpu().numpy(), ref.pair_to_perm)
 
 
-@pytest.mark.parametrize("name", ["nvfp4_ragged", "mxfp4_ragged", "fp8_ragged"])
+@pytest.mark.parametrize("name", ["nvfp4_ragged", "mxfp4_ragged", "fp8_ragged", "nvfp4_aligned",
+                                  "mxfp4_aligned"])
 def test_expert_gemm_and_combine_units(name):
     """Each unit entry point alone, fed the oracle's own routing."""
     w = SMALL[name]
@@ -363,14 +371,14 @@ def test_workspace_reuse_across_batch_sizes():
         assert_close(O.bf16_value(bf16_bits(out)), ref.out, f"reuse T={T}")
 
 
-def _degenerate_layer(fmt):
+def _degenerate_layer(fmt, H=352, I=160):
     """A small layer whose routed experts 0..4 (all tokens route to them: a
     +20 router bias, k = 5) carry degenerate weights: a NaN block scale in
     one down-projection row, a NaN element of an FP8 code, subnormal and zero
     scales, maximum-magnitude codes, an all-zero expert, a zero tensor scale,
     and a NaN block scale in the shared expert's down projection."""
     import dataclasses
-    w = synth.scaled(W["tiny_nvfp4_t4"], name=f"degenerate_{fmt}", T=40, H=352, E=8, I=160,
+    w = synth.scaled(W["tiny_nvfp4_t4"], name=f"degenerate_{fmt}_{H}_{I}", T=40, H=H, E=8, I=I,
                      top_k=5, fmt=fmt, I_shared=96, shared_fmt=synth.FMT_FP8)
     L = layer_for(w)
 
@@ -418,4 +426,17 @@ def test_degenerate_weights(fmt, T):
     x_bits = synth.make_x(w)[:T]
     say(f"[gpu] degenerate weights fmt={fmt} T={T}")
     r = check_layer_against_oracle(L, x_bits, what=f"degenerate {fmt} T={T}")
+    assert np.isnan(r["out"]).any() and np.isfinite(r["out"]).any()
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_NVFP4, synth.FMT_MXFP4])
+@pytest.mark.parametrize("T", [5, 12])
+def test_degenerate_weights_aligned(fmt, T):
+    """The same degenerate values with K a multiple of 128, where the FP4
+    block scales are read by whole chunk (fused decode at T = 5, the
+    small-group expert GEMM at T = 12)."""
+    w, L = _degenerate_layer(fmt, H=512, I=256)
+    x_bits = synth.make_x(w)[:T]
+    say(f"[gpu] degenerate weights (aligned K) fmt={fmt} T={T}")
+    r = check_layer_against_oracle(L, x_bits, what=f"degenerate aligned {fmt} T={T}")
     assert np.isnan(r["out"]).any() and np.isfinite(r["out"]).any()
