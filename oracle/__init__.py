@@ -28,6 +28,7 @@ The router function (softmax, top-k, renormalisation), SwiGLU, the shared
 expert and tie rules are not on the pages; the readings taken are listed in
 the module docstring of :mod:`oracle.layer`.
 
-Submodules: :mod:`oracle.formats` (decoders), :mod:`oracle.layer` (the layer).
+Submodules: :mod:`oracle.formats` (decoders), :mod:`oracle.layer` (the layer),
+:mod:`oracle.lossy` (the opt-in activation-quantizing modes, mirrored).
 """
-from . import formats, layer  # noqa: F401
+from . import formats, layer, lossy  # noqa: F401
