@@ -182,6 +182,75 @@ int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T,
                           void* ws, size_t ws_bytes, float* dbg_logits, int32_t* dbg_ids,
                           float* dbg_w, void* stream);
 
+/* ---- opt-in lossy activation modes ---------------------------------------
+ * The default chain keeps activations BF16.  The pages name activation
+ * quantization only as explicit levers, off by default: NVFP4 W4A4 prefill
+ * behind an opt-in switch (forum thread "DGPP: a GB10-optimized C++/CUDA
+ * inference engine", page 5, the update post), and an FP8 prefill GEMM on
+ * per-token 1x128 E4M3 activations against the checkpoint's 128x128 weight
+ * scales, not bitwise (gitee "dgpp" README, "Execution and performance",
+ * engine.prefill_fp8_gemm).  These modes quantize each expert GEMM input
+ * row from its BF16 form and run the contraction on the gfx950 scaled
+ * FP8/FP4 matrix cores:
+ *   MOE_ACT_MXFP8    (W4A8, MXFP4 experts): E4M3 elements, E8M0 scale per 32 K.
+ *   MOE_ACT_MXFP4    (W4A4, MXFP4 experts): E2M1 elements, E8M0 scale per 32 K.
+ *     MX conversion (OCP Microscaling Formats v1.0): shared exponent
+ *     floor(log2 max|v|) - emax(element) (8 for E4M3, 2 for E2M1), clamped
+ *     to [-127, 127]; elements round to nearest even after v / 2^shared,
+ *     saturating.  All-zero block: scale code 0; a non-finite value: scale
+ *     0xFF and zero codes.
+ *   MOE_ACT_FP8_T128 (FP8 block-128 experts): E4M3 elements, fp32 scale per
+ *     128 K: s = max(amax, 2^-64) / 448, e = RNE(clamp(v / s, +-448)), both
+ *     divisions IEEE fp32; a non-finite value: s = NaN and zero codes.
+ * A mode quantizes the inputs of the projections whose weight format it
+ * names (MXFP4 for the MX modes, FP8_B128 for FP8_T128); other projections
+ * keep the exact chain.  NVFP4 experts have no lossy mode here: their
+ * 16-wide E4M3 block scales do not fit the matrix cores' E8M0-per-32 scale
+ * operand.  Results are deterministic but not those of the exact chain.  */
+#define MOE_ACT_EXACT 0
+#define MOE_ACT_MXFP8 1
+#define MOE_ACT_MXFP4 2
+#define MOE_ACT_FP8_T128 3
+
+/* Quantize bf16 rows for a lossy mode.
+ *   in     bf16 [rows][K], 16-byte aligned; K % 32 == 0.
+ *   codes  MXFP8 / FP8_T128: uint8 E4M3 [rows][K];
+ *          MXFP4: uint8 [rows][K/2], two E2M1 codes per byte, even K in the
+ *          low nibble; 16-byte aligned.
+ *   scales [rows][4*ceil(K/128)] bytes, 4-byte aligned:
+ *          MX modes: E8M0 codes, entry j for K [32j, 32j+32); entries at and
+ *          past K/32 are written 127 (unit scale, padding to whole 128-K
+ *          steps); FP8_T128: fp32 [rows][ceil(K/128)], entry j for
+ *          K [128j, 128j+128).
+ * Returns MOE_ERR_INVALID_ARG for a bad mode, size or pointer. */
+int32_t moe_quantize_act(int32_t mode, const uint16_t* in, int32_t rows, int32_t K,
+                         uint8_t* codes, void* scales, void* stream);
+
+/* moe_expert_gemm on quantized inputs (always the tiled grouped GEMM on the
+ * scaled matrix cores, at any T).  in_codes / in_scales as moe_quantize_act
+ * writes them for the projection's input: x rows [T][H] for op GATE_UP
+ * (routed rows read token perm_to_pair[p]/k), the permuted h rows [T*k][I]
+ * for op DOWN (shared: [T][I_shared]).  The projection's weight format must
+ * be the one the mode names, else MOE_ERR_UNSUPPORTED.  Other arguments and
+ * outputs as moe_expert_gemm. */
+int32_t moe_expert_gemm_q(int32_t mode, int32_t op, const moe_layer_desc* L, int32_t shared,
+                          const int32_t* offsets, const int32_t* perm_to_pair,
+                          const int32_t* active_experts, int32_t T, const uint8_t* in_codes,
+                          const void* in_scales, void* out, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* moe_layer_forward with an activation mode (MOE_ACT_*).  The mode applies to
+ * the prefill lowering (T > 16, the tiled grouped GEMM); decode-sized calls
+ * (T <= 16) stream the weights once per active expert, where quantizing the
+ * few activation rows saves nothing, and compute the exact chain.  A mode
+ * that names no projection format of the layer, or applies to a projection
+ * whose K (cols) is not a multiple of 32, returns MOE_ERR_UNSUPPORTED.
+ * The workspace of moe_workspace_size(L, T) serves every mode.  MOE_ACT_EXACT
+ * is moe_layer_forward. */
+int32_t moe_layer_forward_ex(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
+                             void* ws, size_t ws_bytes, int32_t act_mode, float* dbg_logits,
+                             int32_t* dbg_ids, float* dbg_w, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

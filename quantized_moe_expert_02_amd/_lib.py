@@ -27,9 +27,15 @@ MOE_FMT_FP8_B128 = 3
 MOE_OP_GATE_UP_SWIGLU = 0
 MOE_OP_DOWN = 1
 
+MOE_ACT_EXACT = 0
+MOE_ACT_MXFP8 = 1
+MOE_ACT_MXFP4 = 2
+MOE_ACT_FP8_T128 = 3
+
 EXPORTED = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_validate_layer", "moe_workspace_size",
             "moe_route_topk", "moe_permute_workspace_size", "moe_permute", "moe_expert_gemm",
-            "moe_combine", "moe_layer_forward"]
+            "moe_combine", "moe_layer_forward", "moe_quantize_act", "moe_expert_gemm_q",
+            "moe_layer_forward_ex"]
 
 
 class MoeError(RuntimeError):
@@ -78,6 +84,9 @@ def _load():
         "moe_expert_gemm": (I32, [I32, LP, I32, P, P, P, I32, P, P, P, SZ, P]),
         "moe_combine": (I32, [P, P, P, P, I32, I32, I32, P, P]),
         "moe_layer_forward": (I32, [LP, P, I32, P, P, SZ, P, P, P, P]),
+        "moe_quantize_act": (I32, [I32, P, I32, I32, P, P, P]),
+        "moe_expert_gemm_q": (I32, [I32, I32, LP, I32, P, P, P, I32, P, P, P, P, SZ, P]),
+        "moe_layer_forward_ex": (I32, [LP, P, I32, P, P, SZ, I32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -168,3 +177,25 @@ def moe_layer_forward(L, x, T, out, ws, ws_bytes=None, dbg_logits=None, dbg_ids=
     st = LIB.moe_layer_forward(ctypes.byref(L), _p(x), T, _p(out), _p(ws), wsb, _p(dbg_logits),
                                _p(dbg_ids), _p(dbg_w), _stream(stream))
     return _check(st, "moe_layer_forward") if check else st
+
+
+def moe_layer_forward_ex(L, x, T, out, ws, act_mode, ws_bytes=None, dbg_logits=None, dbg_ids=None,
+                         dbg_w=None, stream=None, check=True):
+    wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    st = LIB.moe_layer_forward_ex(ctypes.byref(L), _p(x), T, _p(out), _p(ws), wsb, act_mode,
+                                  _p(dbg_logits), _p(dbg_ids), _p(dbg_w), _stream(stream))
+    return _check(st, "moe_layer_forward_ex") if check else st
+
+
+def moe_quantize_act(mode, inp, rows, K, codes, scales, stream=None, check=True):
+    st = LIB.moe_quantize_act(mode, _p(inp), rows, K, _p(codes), _p(scales), _stream(stream))
+    return _check(st, "moe_quantize_act") if check else st
+
+
+def moe_expert_gemm_q(mode, op, L, shared, offsets, perm_to_pair, active_experts, T, in_codes,
+                      in_scales, out, ws, ws_bytes=None, stream=None, check=True):
+    wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    st = LIB.moe_expert_gemm_q(mode, op, ctypes.byref(L), shared, _p(offsets), _p(perm_to_pair),
+                               _p(active_experts), T, _p(in_codes), _p(in_scales), _p(out), _p(ws),
+                               wsb, _stream(stream))
+    return _check(st, "moe_expert_gemm_q") if check else st

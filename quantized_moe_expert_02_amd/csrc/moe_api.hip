@@ -80,6 +80,21 @@ WDesc wdesc(const moe_qweight& q) {
   return w;
 }
 
+bool act_mode_valid(int32_t m) {
+  return m == MOE_ACT_MXFP8 || m == MOE_ACT_MXFP4 || m == MOE_ACT_FP8_T128;
+}
+
+// Does lossy mode m quantize the inputs of a projection in weight format f?
+bool mode_applies(int32_t m, int32_t f) {
+  if (m == MOE_ACT_MXFP8 || m == MOE_ACT_MXFP4) return f == MOE_FMT_MXFP4;
+  if (m == MOE_ACT_FP8_T128) return f == MOE_FMT_FP8_B128;
+  return false;
+}
+
+int act_kernel_mode(int32_t m) {
+  return m == MOE_ACT_MXFP8 ? kActMxfp8 : (m == MOE_ACT_MXFP4 ? kActMxfp4 : kActT128);
+}
+
 int32_t check_layer(const moe_layer_desc* L) {
   if (L == nullptr) return MOE_ERR_INVALID_ARG;
   if (L->H <= 0 || L->I <= 0 || L->E <= 0 || L->top_k <= 0) return MOE_ERR_INVALID_ARG;
@@ -116,6 +131,9 @@ struct WsPlan {
   size_t planes, wrt, wsq;
   // fused decode (T <= kDecodeRows): router slice sums
   size_t dpart, dapart;
+  // lossy activation modes (T > kGemvMaxRows): quantized x, h and shared h
+  // (codes sized for E4M3, scales 4 bytes per 128 K per row)
+  size_t xq, xqs, hq, hqs, hsq, hsqs;
 };
 
 constexpr int kDecodeRows = 8;
@@ -172,6 +190,18 @@ WsPlan plan(const moe_layer_desc* L, int T) {
   if (T <= kDecodeRows) {
     p.dpart = take((size_t)p.dp.RS * T * E * 4);
     p.dapart = take((size_t)p.dp.RS * T * E * 4);
+  }
+  p.xq = p.xqs = p.hq = p.hqs = p.hsq = p.hsqs = 0;
+  if (T > kGemvMaxRows) {
+    auto sb = [](int K) { return (size_t)act_scale_pitch(K); };
+    p.xq = take((size_t)T * L->H);
+    p.xqs = take((size_t)T * sb(L->H));
+    p.hq = take((size_t)p.P * L->I);
+    p.hqs = take((size_t)p.P * sb(L->I));
+    if (L->has_shared) {
+      p.hsq = take((size_t)T * L->I_shared);
+      p.hsqs = take((size_t)T * sb(L->I_shared));
+    }
   }
   p.total = o;
   return p;
@@ -277,6 +307,41 @@ int32_t run_experts(int op, const moe_layer_desc* L, int shared, const int* offs
   return hip_status(launch_expert_gemv(op, w0, w1, g, in, out, s));
 }
 
+// The grouped GEMM on quantized inputs (any T).
+int32_t run_experts_q(int32_t mode, int op, const moe_layer_desc* L, int shared, const int* offsets,
+                      const int* perm_to_pair, const int* active, int T, const uint8_t* codes,
+                      const void* scales, void* out, void* ws, const WsPlan& p, bool tiles_ready,
+                      hipStream_t s) {
+  GroupArgs g;
+  g.offsets = offsets;
+  g.perm_to_pair = perm_to_pair;
+  g.topk = L->top_k;
+  g.shared = shared;
+  g.T = T;
+  g.E = L->E;
+  g.max_groups = p.P < L->E ? p.P : L->E;
+  g.act = nullptr;
+  g.n_act = nullptr;
+  if (!shared && !tiles_ready) {
+    hipError_t e = launch_groups_from_offsets(offsets, L->E, at<int>(ws, p.act),
+                                              at<int>(ws, p.nact), kTileM, at<int>(ws, p.tiles),
+                                              at<int>(ws, p.ntiles), p.max_tiles, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  (void)active;
+  WDesc w0, w1;
+  if (op == MOE_OP_GATE_UP_SWIGLU) {
+    w0 = wdesc(shared ? L->sh_gate : L->gate);
+    w1 = wdesc(shared ? L->sh_up : L->up);
+  } else {
+    w0 = wdesc(shared ? L->sh_down : L->down);
+    w1 = w0;
+  }
+  return hip_status(launch_grouped_gemm_q(act_kernel_mode(mode), op, w0, w1, g,
+                                          at<int>(ws, p.tiles), at<int>(ws, p.ntiles),
+                                          p.max_tiles, codes, scales, out, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,11 +441,26 @@ int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pai
                                    static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
-                          void* ws, size_t ws_bytes, float* dbg_logits, int32_t* dbg_ids,
-                          float* dbg_w, void* stream) {
+int32_t moe_layer_forward_ex(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
+                             void* ws, size_t ws_bytes, int32_t act_mode, float* dbg_logits,
+                             int32_t* dbg_ids, float* dbg_w, void* stream) {
   int32_t st = check_layer(L);
   if (st != MOE_OK) return st;
+  if (act_mode != MOE_ACT_EXACT) {
+    if (!act_mode_valid(act_mode)) return MOE_ERR_INVALID_ARG;
+    const bool any = mode_applies(act_mode, L->gate.format) ||
+                     mode_applies(act_mode, L->down.format) ||
+                     (L->has_shared && (mode_applies(act_mode, L->sh_gate.format) ||
+                                        mode_applies(act_mode, L->sh_down.format)));
+    if (!any) return MOE_ERR_UNSUPPORTED;
+    // the quantizer works on whole 32-element blocks of K
+    auto k_ok = [&](const moe_qweight& q) {
+      return !mode_applies(act_mode, q.format) || q.cols % 32 == 0;
+    };
+    if (!k_ok(L->gate) || !k_ok(L->down) ||
+        (L->has_shared && (!k_ok(L->sh_gate) || !k_ok(L->sh_down))))
+      return MOE_ERR_UNSUPPORTED;
+  }
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (x == nullptr || out == nullptr || !aligned(x, 16) || !aligned(out, 16))
@@ -437,23 +517,101 @@ int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T,
   uint16_t* h = at<uint16_t>(ws, p.h);
   float* y = at<float>(ws, p.y);
   const int* active = at<int>(ws, p.nact);
-  if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, x, h, ws, p, true,
-                        s)))
+  // Lossy modes (prefill lowering only): which projections quantize their inputs.
+  const bool lossy = act_mode != MOE_ACT_EXACT && T > kGemvMaxRows;
+  const bool q_gu = lossy && mode_applies(act_mode, L->gate.format);
+  const bool q_d = lossy && mode_applies(act_mode, L->down.format);
+  const bool q_sgu = lossy && L->has_shared && mode_applies(act_mode, L->sh_gate.format);
+  const bool q_sd = lossy && L->has_shared && mode_applies(act_mode, L->sh_down.format);
+  const int km = act_kernel_mode(act_mode);
+  uint8_t* xq = at<uint8_t>(ws, p.xq);
+  void* xqs = at<void>(ws, p.xqs);
+  if ((q_gu || q_sgu) &&
+      (st = hip_status(launch_quantize_act(km, x, T, L->H, xq, xqs, s))) != MOE_OK)
     return st;
-  if ((st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, h, y, ws, p, true, s)))
-    return st;
+  st = q_gu ? run_experts_q(act_mode, MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, xq,
+                            xqs, h, ws, p, true, s)
+            : run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, x, h, ws, p,
+                          true, s);
+  if (st != MOE_OK) return st;
+  if (q_d) {
+    uint8_t* hq = at<uint8_t>(ws, p.hq);
+    void* hqs = at<void>(ws, p.hqs);
+    if ((st = hip_status(launch_quantize_act(km, h, p.P, L->I, hq, hqs, s))) != MOE_OK) return st;
+    st = run_experts_q(act_mode, MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, hq, hqs, y, ws, p,
+                       true, s);
+  } else {
+    st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, h, y, ws, p, true, s);
+  }
+  if (st != MOE_OK) return st;
   float* ys = nullptr;
   if (L->has_shared) {
     uint16_t* hs = at<uint16_t>(ws, p.hs);
     ys = at<float>(ws, p.ys);
-    if ((st = run_experts(MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T, x, hs, ws, p,
-                          true, s)))
-      return st;
-    if ((st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hs, ys, ws, p, true,
-                          s)))
-      return st;
+    st = q_sgu ? run_experts_q(act_mode, MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T,
+                               xq, xqs, hs, ws, p, true, s)
+               : run_experts(MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T, x, hs, ws,
+                             p, true, s);
+    if (st != MOE_OK) return st;
+    if (q_sd) {
+      uint8_t* hsq = at<uint8_t>(ws, p.hsq);
+      void* hsqs = at<void>(ws, p.hsqs);
+      if ((st = hip_status(launch_quantize_act(km, hs, T, L->I_shared, hsq, hsqs, s))) != MOE_OK)
+        return st;
+      st = run_experts_q(act_mode, MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hsq, hsqs, ys,
+                         ws, p, true, s);
+    } else {
+      st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hs, ys, ws, p, true, s);
+    }
+    if (st != MOE_OK) return st;
   }
   return hip_status(launch_combine(y, w, pair2p, ys, T, L->top_k, L->H, out, s));
+}
+
+int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
+                          void* ws, size_t ws_bytes, float* dbg_logits, int32_t* dbg_ids,
+                          float* dbg_w, void* stream) {
+  return moe_layer_forward_ex(L, x, T, out, ws, ws_bytes, MOE_ACT_EXACT, dbg_logits, dbg_ids,
+                              dbg_w, stream);
+}
+
+int32_t moe_quantize_act(int32_t mode, const uint16_t* in, int32_t rows, int32_t K,
+                         uint8_t* codes, void* scales, void* stream) {
+  if (!act_mode_valid(mode) || rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (in == nullptr || codes == nullptr || scales == nullptr || !aligned(in, 16) ||
+      !aligned(codes, 16) || !aligned(scales, 4))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_act(act_kernel_mode(mode), in, rows, K, codes, scales,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_expert_gemm_q(int32_t mode, int32_t op, const moe_layer_desc* L, int32_t shared,
+                          const int32_t* offsets, const int32_t* perm_to_pair,
+                          const int32_t* active_experts, int32_t T, const uint8_t* in_codes,
+                          const void* in_scales, void* out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int32_t st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (!act_mode_valid(mode)) return MOE_ERR_INVALID_ARG;
+  if (op != MOE_OP_GATE_UP_SWIGLU && op != MOE_OP_DOWN) return MOE_ERR_INVALID_ARG;
+  if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
+  if (shared && !L->has_shared) return MOE_ERR_INVALID_ARG;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  const moe_qweight& wq = (op == MOE_OP_GATE_UP_SWIGLU) ? (shared ? L->sh_gate : L->gate)
+                                                        : (shared ? L->sh_down : L->down);
+  if (!mode_applies(mode, wq.format) || wq.cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (in_codes == nullptr || in_scales == nullptr || out == nullptr || !aligned(in_codes, 16) ||
+      !aligned(in_scales, 4) || !aligned(out, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (!shared && (offsets == nullptr || (op == MOE_OP_GATE_UP_SWIGLU && perm_to_pair == nullptr)))
+    return MOE_ERR_INVALID_ARG;
+  const WsPlan p = plan(L, T);
+  if (!shared && (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)))
+    return MOE_ERR_WORKSPACE;
+  return run_experts_q(mode, op, L, shared, offsets, perm_to_pair, active_experts, T, in_codes,
+                       in_scales, out, ws, p, false, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

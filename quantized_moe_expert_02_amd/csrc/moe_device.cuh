@@ -20,6 +20,12 @@ constexpr int kWave = 64;
 
 enum : int { FMT_NVFP4 = 1, FMT_MXFP4 = 2, FMT_FP8 = 3 };
 
+// Activation modes of the expert GEMMs: the exact chain (bf16 inputs) and the
+// opt-in lossy ones (inputs quantized per row: MX E4M3 or E2M1 with an E8M0
+// scale per 32 K; E4M3 with an fp32 scale per 128 K).
+enum : int { kActExact = 0, kActMxfp8 = 1, kActMxfp4 = 2, kActT128 = 3 };
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 // One projection of E stacked experts as the kernels see it.
 struct WDesc {
   int fmt;  // FMT_*

@@ -103,6 +103,23 @@ hipError_t launch_grouped_gemm(int op, const WDesc& w0, const WDesc& w1, const G
                                const int* tiles, const int* n_tiles, int max_tiles,
                                const uint16_t* in, void* out, hipStream_t s);
 
+// ---- opt-in lossy activation modes -----------------------------------------
+// Quantize bf16 rows [rows][K] (K % 32 == 0) for mode kActMxfp8 / kActMxfp4 /
+// kActT128: codes [rows][K] (E4M3) or [rows][K/2] (E2M1, even K in the low
+// nibble); scales MX: uint8 E8M0 [rows][act_scale_pitch(K)] (entries past K/32
+// are 127), T128: fp32 [rows][ceil(K/128)].
+inline int act_scale_pitch(int K) { return 4 * ((K + 127) / 128); }
+hipError_t launch_quantize_act(int mode, const uint16_t* in, int rows, int K, uint8_t* codes,
+                               void* scales, hipStream_t s);
+// Grouped GEMM on the scaled matrix cores over quantized inputs (codes and
+// scales laid out as launch_quantize_act writes them).  Weight format: MXFP4
+// for the MX modes, FP8 block-128 for kActT128.  Same tiles, rows and outputs
+// as launch_grouped_gemm.
+hipError_t launch_grouped_gemm_q(int mode, int op, const WDesc& w0, const WDesc& w1,
+                                 const GroupArgs& g, const int* tiles, const int* n_tiles,
+                                 int max_tiles, const uint8_t* in_codes, const void* in_scales,
+                                 void* out, hipStream_t s);
+
 // ---- fused decode lowering (T <= 8) -----------------------------------------
 struct DecodePlan {
   int RS, CS, down_tiles;
