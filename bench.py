@@ -35,7 +35,17 @@ METRIC = "MoE layer µs & tokens/s; HBM GB/s %peak (decode T=1-8), MFMA %peak (p
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP4_PEAK_TFLOPS = 10100.0
+FP8_PEAK_TFLOPS = 5000.0
 GEMV_MAX_ROWS = 16  # calls with more tokens run the tiled grouped GEMM
+
+# Opt-in lossy activation modes: (C code, arithmetic type, dense MFMA peak of
+# the operand pair in TFLOP/s).  An E4M3 x E2M1 pair runs at the FP8 rate.
+ACT_MODES = {
+    "exact": (0, "bf16", BF16_PEAK_TFLOPS),
+    "mxfp8": (1, "fp8e4m3xfp4e2m1", FP8_PEAK_TFLOPS),
+    "mxfp4": (2, "fp4e2m1", FP4_PEAK_TFLOPS),
+    "fp8_t128": (3, "fp8e4m3", FP8_PEAK_TFLOPS),
+}
 
 
 def log(msg):
@@ -74,6 +84,9 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_t1_nvfp4")
+    ap.add_argument("--act-mode", default="exact", choices=list(ACT_MODES),
+                    help="activation mode of the expert GEMMs (lossy modes are opt-in levers; "
+                         "they apply to the prefill lowering, T > 16)")
     ap.add_argument("--weight-sets", type=int, default=None)
     ap.add_argument("--kernel-launches", type=int, default=192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -86,7 +99,7 @@ def main():
                          "profiles/traffic_<workload>.json")
     args = ap.parse_args()
     if args.pmc_summarize:
-        pmc_summarize(args.workload, *args.pmc_summarize)
+        pmc_summarize(args.workload, args.act_mode, *args.pmc_summarize)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -103,6 +116,14 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     T = w.T
+    mode = args.act_mode
+    mode_code, mode_dtype, mode_peak = ACT_MODES[mode]
+    lossy = mode != "exact" and T > GEMV_MAX_ROWS
+    if mode != "exact" and not ((mode in ("mxfp8", "mxfp4") and w.fmt == synth.FMT_MXFP4) or
+                                (mode == "fp8_t128" and w.fmt == synth.FMT_FP8)):
+        print(f"--act-mode {mode} does not apply to the {w.fmt} routed experts of {w.name}",
+              file=sys.stderr)
+        sys.exit(2)
     nsets = args.weight_sets or w.weight_sets
     steps = args.steps if args.steps is not None else (nsets * 100 if T <= 8 else 200)
     warmup = args.warmup if args.warmup is not None else (nsets * 10 if T <= 8 else 20)
@@ -124,7 +145,7 @@ def main():
     torch.cuda.synchronize()
 
     # one eager call, checked against the oracle's routing
-    moe.moe_layer_forward(base.desc, x, T, out, ws, dbg_ids=ids)
+    moe.moe_layer_forward_ex(base.desc, x, T, out, ws, mode_code, dbg_ids=ids)
     torch.cuda.synchronize()
     ids_np = ids.cpu().numpy()
     from oracle import layer as O
@@ -133,7 +154,7 @@ def main():
     log(f"[bench] routing matches the oracle: {routing_exact}")
 
     if args.pmc_probe:
-        pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws)
+        pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws, mode_code if lossy else 0)
         return
 
     # graph of one pass over the weight sets
@@ -143,12 +164,12 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for i in range(n):
-                moe.moe_layer_forward(sets[i % nsets].desc, x, T, out, ws)
+                moe.moe_layer_forward_ex(sets[i % nsets].desc, x, T, out, ws, mode_code)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
             for i in range(n):
-                moe.moe_layer_forward(sets[i % nsets].desc, x, T, out, ws)
+                moe.moe_layer_forward_ex(sets[i % nsets].desc, x, T, out, ws, mode_code)
         return g
 
     per_graph = nsets if T <= 8 else 1
@@ -186,9 +207,10 @@ def main():
     P = T * k
     offsets, p2, act, h = dominant_inputs(moe, torch, dev, L, ids)
     M = args.kernel_launches
+    launch_gate_up = dominant_launcher(moe, torch, dev, L, T, x, offsets, p2, act, h, ws,
+                                       mode_code if lossy else 0)
     for i in range(min(M, 2 * nsets)):  # warm
-        moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, sets[i % nsets].desc, 0, offsets, p2, act, T,
-                            x, h, ws)
+        launch_gate_up(sets[i % nsets])
     torch.cuda.synchronize()
     # M launches back to back between one pair of events on the launch stream
     # (the current stream); the average includes the dispatch gap between
@@ -199,8 +221,7 @@ def main():
         torch.cuda._sleep(50_000_000)  # let the host queue every launch before the GPU reaches them
     k0.record()
     for i in range(M):
-        moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, sets[i % nsets].desc, 0, offsets, p2, act, T,
-                            x, h, ws)
+        launch_gate_up(sets[i % nsets])
     k1.record()
     torch.cuda.synchronize()
     k_avg_us = k0.elapsed_time(k1) * 1e3 / M
@@ -218,11 +239,18 @@ def main():
                 "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                 "avg_launch_us": round(k_avg_us, 3), "algorithmic_bytes_per_launch": k_bytes}
-    else:
+    elif not lossy:
         # bf16 x bf16 -> fp32 contraction on the matrix cores
         roof = {"kernel": "grouped_gemm_kernel (routed gate/up + SwiGLU)",
                 "bound": "mfma", "achieved": round(k_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(k_avg_us, 3), "algorithmic_flops_per_launch": k_flops,
+                "fp4_peak_frac": round(k_tflops / FP4_PEAK_TFLOPS, 5)}
+    else:
+        # quantized activations x checkpoint codes on the scaled matrix cores
+        roof = {"kernel": "grouped_gemm_q_kernel (routed gate/up + SwiGLU, " + mode + ")",
+                "bound": "mfma", "achieved": round(k_tflops, 2), "peak": mode_peak,
+                "unit": "TFLOP/s", "frac": round(k_tflops / mode_peak, 4), "traffic": None,
                 "avg_launch_us": round(k_avg_us, 3), "algorithmic_flops_per_launch": k_flops,
                 "fp4_peak_frac": round(k_tflops / FP4_PEAK_TFLOPS, 5)}
 
@@ -237,13 +265,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": mode_dtype if lossy else "bf16",
         "data": "synthetic",
         "config": {
             "workload": w.name, "T": T, "H": L.H, "E": L.E, "I": L.I, "top_k": L.top_k,
             "routed_format": w.fmt, "shared": (f"{w.shared_fmt} I={w.I_shared}" if w.I_shared else None),
             "zipf_s": w.zipf_s, "weight_sets": nsets, "global_batch": T, "seq_len": 1,
-            "parallelism": "single-gpu",
+            "parallelism": "single-gpu", "act_mode": mode if lossy else "exact",
         },
         "us_per_layer": round(us_per_layer, 3),
         "layer_algorithmic_bytes": alg_bytes,
@@ -254,12 +282,13 @@ def main():
         "layer_fp4_mfma_frac": round(layer_tflops / FP4_PEAK_TFLOPS, 5),
         "unique_experts": int(len(active)),
         "routing_matches_oracle": routing_exact,
-        "roofline": dict(roof, traffic=load_traffic(w.name, T)),
+        "roofline": dict(roof, traffic=load_traffic(w.name, T, mode if lossy else "exact")),
     }
 
     # ---- CPU baseline: the oracle on a bounded sample ----
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, L, x_bits, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, L, x_bits, args.cpu_seconds,
+                                              mode if lossy else None)
     print(json.dumps(result), flush=True)
 
 
@@ -279,67 +308,88 @@ def dominant_inputs(moe, torch, dev, L, ids):
     return offsets, p2, act, h
 
 
+def dominant_launcher(moe, torch, dev, L, T, x, offsets, p2, act, h, ws, mode_code):
+    """A function launching the routed gate/up kernel on one weight set: the
+    exact chain's, or (lossy mode) the scaled-MFMA one on x quantized once."""
+    if mode_code == 0:
+        return lambda s: moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, s.desc, 0, offsets, p2,
+                                             act, T, x, h, ws)
+    H = L.H
+    codes = torch.empty((T, H // 2 if mode_code == moe.MOE_ACT_MXFP4 else H), dtype=torch.uint8,
+                        device=dev)
+    scales = torch.empty((T, 4 * ((H + 127) // 128)), dtype=torch.uint8, device=dev)
+    moe.moe_quantize_act(mode_code, x, T, H, codes, scales)
+    return lambda s: moe.moe_expert_gemm_q(mode_code, moe.MOE_OP_GATE_UP_SWIGLU, s.desc, 0,
+                                           offsets, p2, act, T, codes, scales, h, ws)
+
+
 PMC_COPY_BYTES = 256 << 20
 PMC_COPIES = 4
 PMC_LAUNCHES = 8
 
 
-def pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws):
+def pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws, mode_code):
     """Dispatches for a counter run: PMC_COPIES plain copies of PMC_COPY_BYTES
     (x * 1 into another buffer; the calibration: bytes per counted KiB), then
     PMC_LAUNCHES launches of
     the dominant kernel, cycling weight sets as the timed run does."""
     T = ids.shape[0]
     offsets, p2, act, h = dominant_inputs(moe, torch, dev, L, ids)
+    launch_gate_up = dominant_launcher(moe, torch, dev, L, T, x, offsets, p2, act, h, ws, mode_code)
     src = torch.ones(PMC_COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(PMC_COPIES):  # an elementwise kernel that reads and writes every byte once
         torch.mul(src, 1, out=dst)
     torch.cuda.synchronize()
     for i in range(PMC_LAUNCHES):
-        moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, sets[(i + 1) % nsets].desc, 0, offsets, p2,
-                            act, T, x, h, ws)
+        launch_gate_up(sets[(i + 1) % nsets])
     torch.cuda.synchronize()
     log(f"[bench] pmc probe: {PMC_COPIES} copies of {PMC_COPY_BYTES} B, "
         f"{PMC_LAUNCHES} dominant-kernel launches")
 
 
-def dominant_kernel_name(w):
+def dominant_kernel_name(w, mode="exact"):
     """Template instance of the routed gate/up kernel for the workload."""
+    if mode != "exact" and w.T > GEMV_MAX_ROWS:
+        return f"grouped_gemm_q_kernel<{ACT_MODES[mode][0]}, 0>"
     fmt = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3}[w.fmt]
     base = "expert_gemv_kernel" if w.T <= GEMV_MAX_ROWS else "grouped_gemm_kernel"
     return f"{base}<{fmt}, 0>"
 
 
-def dominant_sources(T):
+def dominant_sources(T, mode="exact"):
     pkg = os.path.join(ROOT, "quantized_moe_expert_02_amd", "csrc")
     files = ["moe_device.cuh", "gemv_core.cuh"]
-    files += ["expert_gemv.hip"] if T <= GEMV_MAX_ROWS else ["expert_gemm.hip"]
+    if T <= GEMV_MAX_ROWS:
+        files += ["expert_gemv.hip"]
+    else:
+        files += ["expert_gemm.hip"] if mode == "exact" else ["expert_gemm_q.hip"]
     return [os.path.join(pkg, f) for f in files]
 
 
-def source_hash(T):
+def source_hash(T, mode="exact"):
     import hashlib
     hsh = hashlib.sha256()
-    for f in dominant_sources(T):
+    for f in dominant_sources(T, mode):
         with open(f, "rb") as fh:
             hsh.update(fh.read())
     return hsh.hexdigest()[:16]
 
 
-def traffic_path(workload):
-    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def traffic_path(workload, mode="exact"):
+    tag = "" if mode == "exact" else "_" + mode
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
 
 
-def load_traffic(workload, T):
+def load_traffic(workload, T, mode="exact"):
     """Counter-measured HBM bytes per launch of the dominant kernel, if the
     counters were taken on the kernel sources as they are now; else None."""
-    p = traffic_path(workload)
+    p = traffic_path(workload, mode)
     if not os.path.exists(p):
         return None
     with open(p) as fh:
         t = json.load(fh)
-    if t.get("source_hash") != source_hash(T):
+    if t.get("source_hash") != source_hash(T, mode):
         return None
     return t["bytes_per_launch"]
 
@@ -354,7 +404,7 @@ def _pmc_rows(d):
     return rows
 
 
-def pmc_summarize(workload, fetch_dir, write_dir):
+def pmc_summarize(workload, mode, fetch_dir, write_dir):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the --pmc-probe runs,
     scaled by what the same counter reads for the plain copy (which moves
     PMC_COPY_BYTES each way), averaged over the dominant kernel's launches."""
@@ -365,7 +415,7 @@ def pmc_summarize(workload, fetch_dir, write_dir):
         val = lambda r: float(r.get("Counter_Value", r.get("Counter-Value")))  # noqa: E731
         copy = [val(r) for r in rows if "elementwise" in r["Kernel_Name"]
                 and "Fill" not in r["Kernel_Name"]]
-        kname = dominant_kernel_name(w)
+        kname = dominant_kernel_name(w, mode)
         kern = [val(r) for r in rows if r["Kernel_Name"].startswith("void moe::(anonymous namespace)::" + kname)]
         kern = kern[-PMC_LAUNCHES:]  # the probe's own launches come last
         if not copy or not kern:
@@ -375,17 +425,19 @@ def pmc_summarize(workload, fetch_dir, write_dir):
         out[name] = {"copy_kib": kib_copy, "bytes_per_kib": factor,
                      "kernel_kib_avg": sum(kern) / len(kern), "launches": len(kern),
                      "kernel_bytes_avg": factor * sum(kern) / len(kern)}
-    res = {"workload": workload, "kernel": dominant_kernel_name(w), "source_hash": source_hash(w.T),
+    res = {"workload": workload, "act_mode": mode, "kernel": dominant_kernel_name(w, mode),
+           "source_hash": source_hash(w.T, mode),
            "bytes_per_launch": round(out["FETCH_SIZE"]["kernel_bytes_avg"]
                                      + out["WRITE_SIZE"]["kernel_bytes_avg"]),
            "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"]}
-    with open(traffic_path(workload), "w") as fh:
+    with open(traffic_path(workload, mode), "w") as fh:
         json.dump(res, fh, indent=1)
     print(json.dumps(res))
 
 
-def cpu_baseline(w, L, x_bits, budget_s):
+def cpu_baseline(w, L, x_bits, budget_s, mode=None):
     from oracle import layer as O
+    from oracle import lossy as Q
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -397,14 +449,20 @@ def cpu_baseline(w, L, x_bits, budget_s):
         sample = f"full layer calls on the same {T}-token batch and weight set, repeated for ~{budget_s:.0f}s"
         per = T
     else:
-        n = 64
+        # wide experts decode far more weight per sampled token
+        n = 64 if w.H * w.I <= 2048 * 512 else 4
         tokens = list(range(0, T, T // n))[:n]
         sample = f"routing of all {T} tokens plus expert FFNs and combine for {n} sampled tokens"
         per = n
+    if mode is not None:
+        sample += f", activation mode {mode}"
     t0 = time.time()
     done = 0
     while True:
-        O.layer_forward(L, x_bits, tokens=tokens)
+        if mode is None:
+            O.layer_forward(L, x_bits, tokens=tokens)
+        else:
+            Q.layer_forward(L, x_bits, mode, tokens=tokens)
         done += 1
         el = time.time() - t0
         if el >= budget_s or (tokens is not None):

@@ -130,6 +130,12 @@ WORKLOADS = {
         Workload("decode_t8_fp8_wide", T=8, H=6144, E=256, I=2048, top_k=8, fmt=FMT_FP8,
                  I_shared=2048, shared_fmt=FMT_FP8, weight_sets=8,
                  note="wide FP8 block-128 experts, 8 cycled layer weight sets"),
+        Workload("prefill_t8192_mxfp4_zipf", T=8192, H=2048, E=512, I=512, top_k=10,
+                 fmt=FMT_MXFP4, I_shared=512, shared_fmt=FMT_FP8, zipf_s=1.1,
+                 note="prefill chunk, MXFP4 routed experts, uneven expert groups"),
+        Workload("prefill_t8192_fp8_wide", T=8192, H=6144, E=256, I=2048, top_k=8,
+                 fmt=FMT_FP8, I_shared=2048, shared_fmt=FMT_FP8,
+                 note="prefill chunk, wide FP8 block-128 experts"),
         Workload("prefill_t8192_nvfp4_zipf", T=8192, H=2048, E=512, I=512, top_k=10,
                  fmt=FMT_NVFP4, I_shared=512, shared_fmt=FMT_FP8, zipf_s=1.1,
                  note="prefill chunk, uneven expert groups"),
@@ -325,10 +331,18 @@ def make_layer(w: Workload, workers: Optional[int] = None) -> LayerWeights:
     if n > 1 and big:
         import multiprocessing as mp
         pool = ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"))
+    def note(what):  # progress of the long generations, on stderr
+        if big:
+            import sys
+            print(f"[synth] {w.name}: {what} generated", file=sys.stderr, flush=True)
+
     try:
         gate = make_qweight(w.seed, "gate", w.E, w.I, w.H, w.fmt, w.w_std, pool)
+        note("gate")
         up = make_qweight(w.seed, "up", w.E, w.I, w.H, w.fmt, w.w_std, pool)
+        note("up")
         down = make_qweight(w.seed, "down", w.E, w.H, w.I, w.fmt, w.w_std, pool)
+        note("down")
         sh = (None, None, None)
         if w.I_shared:
             sf = w.shared_fmt

@@ -200,6 +200,10 @@ LAYERS = {
                                   shared_fmt=synth.FMT_FP8),
     "fp8_mid": synth.scaled(W["tiny_nvfp4_t4"], name="fp8_mid_q", T=260, H=352, E=4, I=160,
                             top_k=2, fmt=synth.FMT_FP8, I_shared=288, shared_fmt=synth.FMT_FP8),
+    # K multiples of 128: the LDS-DMA kernels (whole steps only)
+    "fp8_aligned": synth.scaled(W["tiny_nvfp4_t4"], name="fp8_aligned_q", T=230, H=512, E=6,
+                                I=256, top_k=2, fmt=synth.FMT_FP8, I_shared=384,
+                                shared_fmt=synth.FMT_FP8),
 }
 
 
@@ -217,7 +221,7 @@ def run_layer_ex(dl, x_bits, mode_code):
 
 @pytest.mark.parametrize("name,mode", [("mxfp4_mid", "mxfp8"), ("mxfp4_mid", "mxfp4"),
                                        ("mxfp4_aligned", "mxfp8"), ("mxfp4_aligned", "mxfp4"),
-                                       ("fp8_mid", "fp8_t128")])
+                                       ("fp8_mid", "fp8_t128"), ("fp8_aligned", "fp8_t128")])
 def test_layer_lossy_modes(name, mode):
     w = LAYERS[name]
     L = layer_for(w)
