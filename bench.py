@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP4_PEAK_TFLOPS = 10100.0
 FP8_PEAK_TFLOPS = 5000.0
-GEMV_MAX_ROWS = 16  # calls with more tokens run the tiled grouped GEMM
+GEMV_MAX_ROWS = 64  # calls with more tokens run the tiled grouped GEMM
 
 # Opt-in lossy activation modes: (C code, arithmetic type, dense MFMA peak of
 # the operand pair in TFLOP/s).  An E4M3 x E2M1 pair runs at the FP8 rate.
@@ -86,7 +86,7 @@ def main():
     ap.add_argument("--workload", default="decode_t1_nvfp4")
     ap.add_argument("--act-mode", default="exact", choices=list(ACT_MODES),
                     help="activation mode of the expert GEMMs (lossy modes are opt-in levers; "
-                         "they apply to the prefill lowering, T > 16)")
+                         "they apply to the prefill lowering, T > 64)")
     ap.add_argument("--weight-sets", type=int, default=None)
     ap.add_argument("--kernel-launches", type=int, default=192)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -156,8 +156,9 @@ int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, in
  * Accumulation is fp32; products of the decoded weight and the bf16 input are
  * exact.  The intermediate h is BF16 (activations stay BF16, forum opening
  * post).  The kernel variant follows the row count (row-aware lowering, gitee
- * "dgpp" README, "Highlights"): groups of up to 16 rows stream weights once
- * per group, larger groups run as tiled grouped GEMM. */
+ * "dgpp" README, "Highlights"): calls with T <= 64 stream each active
+ * expert's weights with its own blocks, in passes of 16 rows; larger calls run
+ * the tiled grouped GEMM. */
 int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
                         const int32_t* offsets, const int32_t* perm_to_pair,
                         const int32_t* active_experts, int32_t T, const uint16_t* in, void* out,
@@ -240,8 +241,8 @@ int32_t moe_expert_gemm_q(int32_t mode, int32_t op, const moe_layer_desc* L, int
                           void* stream);
 
 /* moe_layer_forward with an activation mode (MOE_ACT_*).  The mode applies to
- * the prefill lowering (T > 16, the tiled grouped GEMM); decode-sized calls
- * (T <= 16) stream the weights once per active expert, where quantizing the
+ * the prefill lowering (T > 64, the tiled grouped GEMM); decode-sized calls
+ * (T <= 64) stream the weights once per active expert, where quantizing the
  * few activation rows saves nothing, and compute the exact chain.  A mode
  * that names no projection format of the layer, or applies to a projection
  * whose K (cols) is not a multiple of 32, returns MOE_ERR_UNSUPPORTED.

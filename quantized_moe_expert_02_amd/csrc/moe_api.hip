@@ -139,10 +139,12 @@ struct WsPlan {
 constexpr int kDecodeRows = 8;
 
 constexpr int kTileM = kGemmTileM;  // rows per grouped-GEMM tile
-// Calls with at most this many tokens have no group larger than one GEMV
-// pass (a token picks an expert at most once) and stream each expert's
-// weights once; larger calls run the tiled grouped GEMM.
-constexpr int kGemvMaxRows = 16;
+// Calls with at most this many tokens run the expert GEMV lowering: each
+// active expert's weights are streamed by its own blocks, in passes of 16
+// rows (a token picks an expert at most once, so a group has at most this
+// many rows; the passes after the first read the weights from L2); larger
+// calls run the tiled grouped GEMM.
+constexpr int kGemvMaxRows = 64;
 // The matrix-core router's error bound assumes H * 2^-23 << 1.
 constexpr int kMfmaRouterMaxH = 1 << 16;
 

@@ -12,6 +12,8 @@ namespace moe {
 // Rows of the router per partial-sum slice and experts per block.
 constexpr int kRouterCols = 32;
 constexpr int kRouterTokens = 8;
+// Batches of at most this many tokens take the sliced router.
+constexpr int kRouterSlicedRows = 64;
 constexpr int kMaxExperts = 1024;  // top-k keeps up to 16 logits per lane
 constexpr int kMaxTopK = 32;
 

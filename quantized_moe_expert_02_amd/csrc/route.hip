@@ -22,10 +22,11 @@ namespace moe {
 
 RouterPlan router_plan(int T, int H, int E) {
   RouterPlan p;
-  // One slice: each block sums the whole contraction for its 32 experts and
-  // 8 tokens, so the partial is the full sum.
-  (void)T;
-  p.RH = H;
+  // Up to kRouterSlicedRows tokens: 128-row slices, so that the (slice x 32
+  // experts x 8 tokens) blocks fill the chip; the top-k adds the slices.
+  // Larger batches (which take this router only when H is too large for the
+  // matrix-core one): one slice, each block summing the whole contraction.
+  p.RH = (T <= kRouterSlicedRows) ? 128 : H;
   p.RS = (H + p.RH - 1) / p.RH;
   p.CS = (E + kRouterCols - 1) / kRouterCols;
   return p;
@@ -106,6 +107,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   __shared__ BlockTopkSmem sm;
   __shared__ float amax_w[kTopkThreads / kWave];
+  __shared__ float bias_w[kTopkThreads / kWave];
   const int t = blockIdx.x, E = a.E;
   if (a.mode == 0) {
     for (int e = threadIdx.x; e < E; e += blockDim.x)
@@ -120,23 +122,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
   }
   // Error bound of the fast logits (mode 1): the router kernel's per-block
-  // factors (amax) times its scale; see TopkArgs.
+  // factors (amax) times its scale; see TopkArgs.  Each slice's fp32
+  // rounding errs by at most 2^-24 of that slice's sum of |x||w|, so the
+  // bound adds, over slices, the maximum over column blocks.
   float m = 0.f;
   if (a.mode == 1) {
-    for (int i = threadIdx.x; i < a.RS * a.CS; i += blockDim.x) {
-      const int r = i / a.CS, c = i % a.CS;
-      m = fmaxf(m, a.amax[((size_t)r * a.CS + c) * a.T + t]);
+    for (int r = threadIdx.x; r < a.RS; r += blockDim.x) {
+      float mr = 0.f;
+      for (int c = 0; c < a.CS; ++c) mr = fmaxf(mr, a.amax[((size_t)r * a.CS + c) * a.T + t]);
+      m += mr;
     }
-    if (a.bias != nullptr)
-      for (int e = threadIdx.x; e < E; e += blockDim.x) m = fmaxf(m, fabsf(a.bias[e]));
   }
-  m = wave_max_f(m);
-  if ((threadIdx.x & (kWave - 1)) == 0) amax_w[threadIdx.x / kWave] = m;
+  m = wave_sum_f(m);
+  float mb = 0.f;
+  if (a.mode == 1 && a.bias != nullptr)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) mb = fmaxf(mb, fabsf(a.bias[e]));
+  mb = wave_max_f(mb);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    amax_w[threadIdx.x / kWave] = m;
+    bias_w[threadIdx.x / kWave] = mb;
+  }
   __syncthreads();
-  float am = 0.f;
-  for (int i = 0; i < (int)(blockDim.x / kWave); ++i) am = fmaxf(am, amax_w[i]);
-  // The max over column blocks (and slices) bounds every expert of the
-  // token; |bias| joins the maximum as a safe over-estimate of the float64
+  float am = 0.f, bm = 0.f;
+  for (int i = 0; i < (int)(blockDim.x / kWave); ++i) {
+    am += amax_w[i];
+    bm = fmaxf(bm, bias_w[i]);
+  }
+  am += bm;
+  // The sum over slices of the max over column blocks bounds every expert
+  // of the token; max |bias| is added as a safe over-estimate of the float64
   // bias addition.
   BlockTopkArgs ta;
   ta.E = E;

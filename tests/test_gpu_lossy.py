@@ -237,7 +237,7 @@ def test_layer_lossy_modes(name, mode):
 
 
 def test_layer_mode_small_batches_are_exact():
-    """T <= 16: the mode does not apply; the result is moe_layer_forward's, bit for bit."""
+    """T <= 64: the mode does not apply; the result is moe_layer_forward's, bit for bit."""
     w = synth.scaled(LAYERS["mxfp4_mid"], name="mxfp4_small_q", T=12)
     dl = device_layer(layer_for(w))
     x_bits = synth.make_x(w)

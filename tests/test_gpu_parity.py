@@ -82,6 +82,35 @@ def test_layer_decode_fp8_wide_sampled():
     say(f"[gpu] fp8 wide: rel={r['rel']:.2e} worst={r['worst']:.2e}")
 
 
+# The 9-64 row band (speculative-verify and batched-decode sizes): sliced
+# router, block top-k, expert GEMV in 16-row passes (groups above 16 rows
+# under the Zipf router), shared expert over up to 4 passes.
+BAND = {
+    "nvfp4_t24": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t24", T=24, H=352, E=24, I=160,
+                              top_k=3, I_shared=96, shared_fmt=synth.FMT_FP8, zipf_s=1.1),
+    "mxfp4_t40": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp4_t40", T=40, H=512, E=16, I=256,
+                              top_k=4, fmt=synth.FMT_MXFP4, I_shared=128,
+                              shared_fmt=synth.FMT_MXFP4, zipf_s=1.1),
+    "fp8_t64": synth.scaled(W["tiny_nvfp4_t4"], name="fp8_t64", T=64, H=336, E=8, I=144,
+                            top_k=2, fmt=synth.FMT_FP8, I_shared=272, shared_fmt=synth.FMT_FP8,
+                            zipf_s=1.1),
+    "nvfp4_t64_decode_shape": synth.scaled(W["decode_t8_nvfp4_zipf"], name="nvfp4_t64_band",
+                                           T=64, weight_sets=1),
+}
+
+
+@pytest.mark.parametrize("name", list(BAND))
+def test_layer_row_band(name):
+    w = BAND[name]
+    say(f"[gpu] layer {name}: T={w.T} H={w.H} E={w.E} I={w.I} k={w.top_k} fmt={w.fmt}")
+    tokens = None if w.H * w.E <= 512 * 64 else [0, 13, 31, 47, 63]
+    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), tokens=tokens, what=name)
+    counts = np.bincount(r["ids"].reshape(-1), minlength=w.E)
+    say(f"[gpu] layer {name}: rel={r['rel']:.2e} worst={r['worst']:.2e} max group={counts.max()}")
+    if w.E <= 24:
+        assert counts.max() > 16                 # a group takes more than one 16-row pass
+
+
 @pytest.mark.parametrize("name", list(MID))
 def test_layer_grouped_gemm(name):
     w = MID[name]
@@ -378,7 +407,7 @@ def _degenerate_layer(fmt, H=352, I=160):
     scales, maximum-magnitude codes, an all-zero expert, a zero tensor scale,
     and a NaN block scale in the shared expert's down projection."""
     import dataclasses
-    w = synth.scaled(W["tiny_nvfp4_t4"], name=f"degenerate_{fmt}_{H}_{I}", T=40, H=H, E=8, I=I,
+    w = synth.scaled(W["tiny_nvfp4_t4"], name=f"degenerate_{fmt}_{H}_{I}", T=80, H=H, E=8, I=I,
                      top_k=5, fmt=fmt, I_shared=96, shared_fmt=synth.FMT_FP8)
     L = layer_for(w)
 
@@ -417,10 +446,10 @@ def _degenerate_layer(fmt, H=352, I=160):
 
 
 @pytest.mark.parametrize("fmt", [synth.FMT_NVFP4, synth.FMT_MXFP4, synth.FMT_FP8])
-@pytest.mark.parametrize("T", [5, 12, 40])
+@pytest.mark.parametrize("T", [5, 12, 40, 80])
 def test_degenerate_weights(fmt, T):
     """NaN, subnormal, zero and extreme checkpoint values through the decode
-    (T <= 8), small-group (T <= 16) and grouped-GEMM paths: same NaN pattern
+    (T <= 8), expert-GEMV (T <= 64) and grouped-GEMM paths: same NaN pattern
     as the oracle, the finite outputs within tolerance."""
     w, L = _degenerate_layer(fmt)
     x_bits = synth.make_x(w)[:T]
