@@ -149,7 +149,10 @@ int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, in
  *     token perm_to_pair[p]/k of `in` (x bf16 [T][H]); for op DOWN the input
  *     row is p of `in` (h bf16 [T*k][I]).  Output row p in permuted order.
  *   active_experts: routed only, the [E+1] list moe_permute writes (count,
- *     then ids); NULL derives it from `offsets` with one extra launch.
+ *     then ids), or NULL.  With T <= 64 and a list, one block row per active
+ *     expert takes its whole group; otherwise the call derives a list of row
+ *     chunks from `offsets` with one extra launch (16-row chunks of a group
+ *     run in parallel blocks for T <= 64, 128-row tiles above).
  *   shared = 1: the shared expert over T rows of `in`; offsets, perm_to_pair
  *     and active_experts unused.
  *   out: GATE_UP -> bf16 [rows][I or I_shared]; DOWN -> fp32 [rows][H].
@@ -157,8 +160,8 @@ int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, in
  * exact.  The intermediate h is BF16 (activations stay BF16, forum opening
  * post).  The kernel variant follows the row count (row-aware lowering, gitee
  * "dgpp" README, "Highlights"): calls with T <= 64 stream each active
- * expert's weights with its own blocks, in passes of 16 rows; larger calls run
- * the tiled grouped GEMM. */
+ * expert's weights with its own blocks, 16 rows per pass; larger calls run the
+ * tiled grouped GEMM. */
 int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
                         const int32_t* offsets, const int32_t* perm_to_pair,
                         const int32_t* active_experts, int32_t T, const uint16_t* in, void* out,

@@ -44,6 +44,9 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
   const int rb = blockIdx.x;
   const int T = a.T, H = a.H, E = a.E;
   const int cs = rb / a.RS, rs = rb % a.RS;
+  // token group: tokens t0 .. t0 + nt - 1 (batches above 8 tokens launch
+  // one group of 8 per grid row)
+  const int t0 = blockIdx.y * kTmax, nt = min(kTmax, T - t0);
   const int col = threadIdx.x & 31, rg = threadIdx.x >> 5;
   const int e = cs * kRouterCols + col;
   const int h0 = rs * kRH, nh = min(kRH, H - h0);
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
   }
   for (int i = threadIdx.x; i < kTmax * kRH; i += 256) {
     const int t = i / kRH, h = i % kRH;
-    sm.xs[t][h] = (t < T && h < nh) ? bf16_to_f32(a.x[(size_t)t * H + h0 + h]) : 0.f;
+    sm.xs[t][h] = (t < nt && h < nh) ? bf16_to_f32(a.x[(size_t)(t0 + t) * H + h0 + h]) : 0.f;
   }
   __syncthreads();
   double acc[kTmax];
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
     const float wa = fabsf(wv[j]);
 #pragma unroll
     for (int t = 0; t < kTmax; ++t) {
-      if (t < T) {  // bf16 * fp32 is exact in float64
+      if (t < nt) {  // bf16 * fp32 is exact in float64
         acc[t] = fma(static_cast<double>(sm.xs[t][h]), wd, acc[t]);
         aa[t] = fmaf(fabsf(sm.xs[t][h]), wa, aa[t]);
       }
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
     sm.reda[rg][t][col] = aa[t];
   }
   __syncthreads();
-  if (rg < T && e < E) {  // thread (t = rg, col) folds the 8 row groups
+  if (rg < nt && e < E) {  // thread (t = rg, col) folds the 8 row groups
     const int t = rg;
     double s = 0.0;
     float av = 0.f;
@@ -94,8 +97,8 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
       s += sm.red[g][t][col];
       av += sm.reda[g][t][col];
     }
-    a.part[((size_t)rs * T + t) * E + e] = static_cast<float>(s);
-    a.apart[((size_t)rs * T + t) * E + e] = av;
+    a.part[((size_t)rs * T + t0 + t) * E + e] = static_cast<float>(s);
+    a.apart[((size_t)rs * T + t0 + t) * E + e] = av;
   }
 }
 
@@ -399,6 +402,13 @@ DecodePlan decode_plan(int T, int H, int E) {
   p.down_tiles = (H + gemv_rows_per_block<kOpDown>() - 1) / gemv_rows_per_block<kOpDown>();
   (void)T;
   return p;
+}
+
+hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.RS * a.CS, (a.T + kTmax - 1) / kTmax);
+  hipError_t err = launch(decode_router_kernel, grid, dim3(256), 0, s, a);
+  if (err != hipSuccess) return err;
+  return launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {

@@ -123,7 +123,7 @@ int32_t check_layer(const moe_layer_desc* L) {
 struct WsPlan {
   RouterPlan rp;
   DecodePlan dp;
-  int P, NB, max_tiles;
+  int P, NB, max_tiles, tile_m;  // tile list: chunks of tile_m rows (GEMM tile or GEMV pass)
   size_t part, amax, ids, w, counts, offsets, p2pair, pair2p, hist, act, nact, tiles, ntiles, h,
       hs, y, ys, total;
   // matrix-core router (T > kGemvMaxRows): split router planes and w^2 sums
@@ -154,7 +154,8 @@ WsPlan plan(const moe_layer_desc* L, int T) {
   p.rp = router_plan(T, L->H, E);
   p.P = T * k;
   p.NB = (p.P + kPermChunk - 1) / kPermChunk;
-  p.max_tiles = p.P / kTileM + (p.P < E ? p.P : E) + 1;
+  p.tile_m = (T > kGemvMaxRows) ? kTileM : kGemvChunk;
+  p.max_tiles = p.P / p.tile_m + (p.P < E ? p.P : E) + 1;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -189,7 +190,7 @@ WsPlan plan(const moe_layer_desc* L, int T) {
     p.wsq = take(router_mfma_wsq_count(L->H, E) * 8);
   }
   p.dpart = p.dapart = 0;
-  if (T <= kDecodeRows) {
+  if (T <= kRouterSlicedRows) {  // decode router slices (fused decode and the sliced router)
     p.dpart = take((size_t)p.dp.RS * T * E * 4);
     p.dapart = take((size_t)p.dp.RS * T * E * 4);
   }
@@ -238,6 +239,27 @@ int32_t run_route(const moe_layer_desc* L, const uint16_t* x, float* logits, int
     a.part = logits;
     a.RS = 1;
     a.wave = T > kGemvMaxRows;
+  } else if (T <= kRouterSlicedRows) {
+    // the decode router (128-row slices of fp64 sums, token groups of 8) and
+    // the decode top-k, certified with the per-expert sums of |x||w|
+    DecodeArgs d;
+    std::memset(&d, 0, sizeof(d));
+    d.x = x;
+    d.T = T;
+    d.H = L->H;
+    d.E = L->E;
+    d.k = L->top_k;
+    d.renorm = L->renormalize;
+    d.wr = L->router_w;
+    d.bias = L->router_bias;
+    d.RS = p.dp.RS;
+    d.CS = p.dp.CS;
+    d.part = at<float>(ws, p.dpart);
+    d.apart = at<float>(ws, p.dapart);
+    d.logits_out = logits;
+    d.ids = ids;
+    d.w = w;
+    return hip_status(launch_decode_route(d, s));
   } else {
     a.mode = 1;
     a.part = at<float>(ws, p.part);
@@ -279,11 +301,13 @@ int32_t run_experts(int op, const moe_layer_desc* L, int shared, const int* offs
   g.offsets = offsets;
   g.perm_to_pair = perm_to_pair;
   const bool gemm = T > kGemvMaxRows;
-  const bool groups_ready = shared || (gemm ? tiles_ready : active != nullptr);
-  if (gemm && !shared) active = at<int>(ws, p.nact);
-  if (active == nullptr && !shared) active = at<int>(ws, p.nact);
-  g.act = active ? active + 1 : nullptr;
-  g.n_act = active;
+  // The GEMV takes a caller's active-expert list as is (a block row per
+  // group, no extra launch); otherwise both lowerings use the tile list,
+  // built from offsets unless the layer's permute wrote it.
+  const bool by_groups = !gemm && !shared && !tiles_ready && active != nullptr;
+  const bool groups_ready = shared || tiles_ready || by_groups;
+  g.act = by_groups ? active + 1 : nullptr;
+  g.n_act = by_groups ? active : nullptr;
   g.topk = L->top_k;
   g.shared = shared;
   g.T = T;
@@ -291,7 +315,7 @@ int32_t run_experts(int op, const moe_layer_desc* L, int shared, const int* offs
   g.max_groups = p.P < L->E ? p.P : L->E;
   if (!shared && !groups_ready) {
     hipError_t e = launch_groups_from_offsets(offsets, L->E, at<int>(ws, p.act),
-                                              at<int>(ws, p.nact), kTileM, at<int>(ws, p.tiles),
+                                              at<int>(ws, p.nact), p.tile_m, at<int>(ws, p.tiles),
                                               at<int>(ws, p.ntiles), p.max_tiles, s);
     if (e != hipSuccess) return hip_status(e);
   }
@@ -306,7 +330,10 @@ int32_t run_experts(int op, const moe_layer_desc* L, int shared, const int* offs
   if (gemm)
     return hip_status(launch_grouped_gemm(op, w0, w1, g, at<int>(ws, p.tiles),
                                           at<int>(ws, p.ntiles), p.max_tiles, in, out, s));
-  return hip_status(launch_expert_gemv(op, w0, w1, g, in, out, s));
+  if (by_groups)
+    return hip_status(launch_expert_gemv(op, w0, w1, g, nullptr, nullptr, 0, in, out, s));
+  return hip_status(launch_expert_gemv(op, w0, w1, g, at<int>(ws, p.tiles), at<int>(ws, p.ntiles),
+                                       p.max_tiles, in, out, s));
 }
 
 // The grouped GEMM on quantized inputs (any T).
@@ -324,10 +351,14 @@ int32_t run_experts_q(int32_t mode, int op, const moe_layer_desc* L, int shared,
   g.max_groups = p.P < L->E ? p.P : L->E;
   g.act = nullptr;
   g.n_act = nullptr;
+  // This GEMM always runs on 128-row tiles (a ready tile list exists only on
+  // the layer's prefill lowering, where the plan's tiles are 128 rows); the
+  // workspace's list holds at least this many entries.
+  const int max_tiles = p.P / kTileM + (p.P < L->E ? p.P : L->E) + 1;
   if (!shared && !tiles_ready) {
     hipError_t e = launch_groups_from_offsets(offsets, L->E, at<int>(ws, p.act),
                                               at<int>(ws, p.nact), kTileM, at<int>(ws, p.tiles),
-                                              at<int>(ws, p.ntiles), p.max_tiles, s);
+                                              at<int>(ws, p.ntiles), max_tiles, s);
     if (e != hipSuccess) return hip_status(e);
   }
   (void)active;
@@ -341,7 +372,7 @@ int32_t run_experts_q(int32_t mode, int op, const moe_layer_desc* L, int shared,
   }
   return hip_status(launch_grouped_gemm_q(act_kernel_mode(mode), op, w0, w1, g,
                                           at<int>(ws, p.tiles), at<int>(ws, p.ntiles),
-                                          p.max_tiles, codes, scales, out, s));
+                                          max_tiles, codes, scales, out, s));
 }
 
 }  // namespace
@@ -513,7 +544,7 @@ int32_t moe_layer_forward_ex(const moe_layer_desc* L, const uint16_t* x, int32_t
   int* pair2p = at<int>(ws, p.pair2p);
   if ((st = hip_status(launch_permute(ids, T, L->top_k, L->E, at<int>(ws, p.counts), offsets,
                                       p2pair, pair2p, at<int>(ws, p.hist), at<int>(ws, p.act),
-                                      at<int>(ws, p.nact), kTileM, at<int>(ws, p.tiles),
+                                      at<int>(ws, p.nact), p.tile_m, at<int>(ws, p.tiles),
                                       at<int>(ws, p.ntiles), p.max_tiles, s))) != MOE_OK)
     return st;
   uint16_t* h = at<uint16_t>(ws, p.h);

@@ -95,7 +95,14 @@ struct GroupArgs {
   int E;
   int max_groups;  // grid bound on active experts
 };
+// Expert GEMV over chunks of at most kGemvChunk rows: routed chunks come from
+// the tile list of launch_permute / launch_groups_from_offsets built with
+// tile_m = kGemvChunk (int2 (expert, first permuted row)), or, with tiles ==
+// nullptr, one block row per active expert of g.act / g.n_act takes the
+// whole group; the shared expert (g.shared) is cut into chunks of its T rows.
+constexpr int kGemvChunk = 16;
 hipError_t launch_expert_gemv(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
+                              const int* tiles, const int* n_tiles, int max_tiles,
                               const uint16_t* in, void* out, hipStream_t s);
 // Tiled grouped GEMM (row groups of any size) over the tile list of
 // launch_permute / launch_groups_from_offsets: tiles int2 (expert, first
@@ -146,6 +153,10 @@ struct DecodeArgs {
   uint16_t* out;      // [T][H]
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Routing alone with the decode router (128-row slices, token groups of 8)
+// and the decode top-k, for batches up to kRouterSlicedRows tokens: reads x,
+// wr, bias; writes part/apart (workspace), logits_out (optional), ids, w.
+hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------------
 hipError_t launch_combine(const float* y, const float* w, const int* pair_to_perm, const float* ys,
