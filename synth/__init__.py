@@ -127,6 +127,12 @@ WORKLOADS = {
         Workload("decode_t8_mxfp4_zipf", T=8, H=2048, E=512, I=512, top_k=10, fmt=FMT_MXFP4,
                  I_shared=512, shared_fmt=FMT_FP8, zipf_s=1.1, weight_sets=48,
                  note="8 concurrent sequences, MXFP4 routed experts"),
+        Workload("decode_t32_nvfp4_zipf", T=32, H=2048, E=512, I=512, top_k=10, fmt=FMT_NVFP4,
+                 I_shared=512, shared_fmt=FMT_FP8, zipf_s=1.1, weight_sets=48,
+                 note="32 rows (batched decode / speculative verify), Zipf expert popularity"),
+        Workload("decode_t64_nvfp4_zipf", T=64, H=2048, E=512, I=512, top_k=10, fmt=FMT_NVFP4,
+                 I_shared=512, shared_fmt=FMT_FP8, zipf_s=1.1, weight_sets=48,
+                 note="64 rows (batched decode / speculative verify), Zipf expert popularity"),
         Workload("decode_t8_fp8_wide", T=8, H=6144, E=256, I=2048, top_k=8, fmt=FMT_FP8,
                  I_shared=2048, shared_fmt=FMT_FP8, weight_sets=8,
                  note="wide FP8 block-128 experts, 8 cycled layer weight sets"),
