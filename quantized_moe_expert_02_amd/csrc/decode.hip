@@ -323,6 +323,8 @@ __device__ __forceinline__ f32x4 gemv16_row(const WDesc& w, int e, int n0, const
 constexpr int kDcCols = 16;
 constexpr int kDcMaxWaves = 12;  // one wavefront per slot up to 12 slots (168 VGPRs each)
 
+// RFMT / SFMT: the formats of the routed and the shared down projections
+// (a layer's down projections may use another format than its gate/up).
 template <int RFMT, int SFMT>
 __global__ __launch_bounds__(kDcMaxWaves * kWave) void decode_down_combine_kernel(DecodeArgs a) {
   __shared__ float yp[kMaxTopK + 1][kDcCols];
@@ -361,34 +363,50 @@ __global__ __launch_bounds__(kDcMaxWaves * kWave) void decode_down_combine_kerne
   }
 }
 
-template <int RFMT, int SFMT>
-hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
-  const int nrb = a.RS * a.CS;
-  const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
-  hipError_t err = launch(decode_router_kernel, dim3(nrb), dim3(256), 0, s, a);
-  if (err != hipSuccess) return err;
-  err = launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
-  if (err != hipSuccess) return err;
-  const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
-  err = launch(decode_gateup_kernel<RFMT, SFMT>, dim3(nsg + ngu), dim3(kWave * kGuWK), 0, s, a);
-  if (err != hipSuccess) return err;
-  // One wavefront per slot (one round trip per block) when the grid is
-  // smaller than the GPU; otherwise 8 per block keep more blocks resident.
-  const int nslots = a.k + ((SFMT != 0) ? 1 : 0);
-  const int nblocks = a.T * (a.H / kDcCols);
-  const int dcw = (nblocks < 256) ? (nslots < kDcMaxWaves ? nslots : kDcMaxWaves)
-                                  : (nslots < 8 ? nslots : 8);
-  return launch(decode_down_combine_kernel<RFMT, SFMT>, dim3(a.T * (a.H / kDcCols)),
-                dim3(dcw * kWave), 0, s, a);
+// Gate/up formats (routed, shared) pick the gate/up kernel; down formats
+// (routed, shared) pick the down-combine kernel.
+struct GateUpLaunch {
+  template <int RFMT, int SFMT>
+  static hipError_t run(const DecodeArgs& a, hipStream_t s) {
+    const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
+    const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
+    return launch(decode_gateup_kernel<RFMT, SFMT>, dim3(nsg + ngu), dim3(kWave * kGuWK), 0, s,
+                  a);
+  }
+};
+
+struct DownLaunch {
+  template <int RFMT, int SFMT>
+  static hipError_t run(const DecodeArgs& a, hipStream_t s) {
+    // One wavefront per slot (one round trip per block) when the grid is
+    // smaller than the GPU; otherwise 8 per block keep more blocks resident.
+    const int nslots = a.k + ((SFMT != 0) ? 1 : 0);
+    const int nblocks = a.T * (a.H / kDcCols);
+    const int dcw = (nblocks < 256) ? (nslots < kDcMaxWaves ? nslots : kDcMaxWaves)
+                                    : (nslots < 8 ? nslots : 8);
+    return launch(decode_down_combine_kernel<RFMT, SFMT>, dim3(nblocks), dim3(dcw * kWave), 0, s,
+                  a);
+  }
+};
+
+// (routed format, shared format or 0) -> L::run<RFMT, SFMT>
+template <class L, int RFMT>
+hipError_t by_shared_format(int sfmt, const DecodeArgs& a, hipStream_t s) {
+  switch (sfmt) {
+    case 0: return L::template run<RFMT, 0>(a, s);
+    case FMT_NVFP4: return L::template run<RFMT, FMT_NVFP4>(a, s);
+    case FMT_MXFP4: return L::template run<RFMT, FMT_MXFP4>(a, s);
+    case FMT_FP8: return L::template run<RFMT, FMT_FP8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-template <int RFMT>
-hipError_t launch_r(int sfmt, const DecodeArgs& a, hipStream_t s) {
-  switch (sfmt) {
-    case 0: return launch4<RFMT, 0>(a, s);
-    case FMT_NVFP4: return launch4<RFMT, FMT_NVFP4>(a, s);
-    case FMT_MXFP4: return launch4<RFMT, FMT_MXFP4>(a, s);
-    case FMT_FP8: return launch4<RFMT, FMT_FP8>(a, s);
+template <class L>
+hipError_t by_formats(int rfmt, int sfmt, const DecodeArgs& a, hipStream_t s) {
+  switch (rfmt) {
+    case FMT_NVFP4: return by_shared_format<L, FMT_NVFP4>(sfmt, a, s);
+    case FMT_MXFP4: return by_shared_format<L, FMT_MXFP4>(sfmt, a, s);
+    case FMT_FP8: return by_shared_format<L, FMT_FP8>(sfmt, a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -412,13 +430,13 @@ hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  const int sfmt = a.has_shared ? a.sg.fmt : 0;
-  switch (a.gate.fmt) {
-    case FMT_NVFP4: return launch_r<FMT_NVFP4>(sfmt, a, s);
-    case FMT_MXFP4: return launch_r<FMT_MXFP4>(sfmt, a, s);
-    case FMT_FP8: return launch_r<FMT_FP8>(sfmt, a, s);
-    default: return hipErrorInvalidValue;
-  }
+  hipError_t err = launch(decode_router_kernel, dim3(a.RS * a.CS), dim3(256), 0, s, a);
+  if (err != hipSuccess) return err;
+  err = launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
+  if (err != hipSuccess) return err;
+  err = by_formats<GateUpLaunch>(a.gate.fmt, a.has_shared ? a.sg.fmt : 0, a, s);
+  if (err != hipSuccess) return err;
+  return by_formats<DownLaunch>(a.down.fmt, a.has_shared ? a.sd.fmt : 0, a, s);
 }
 
 }  // namespace moe

@@ -104,6 +104,9 @@ class Workload:
     fmt: str
     I_shared: int = 0
     shared_fmt: Optional[str] = None
+    # down projections in another format than gate/up (None: the same)
+    down_fmt: Optional[str] = None
+    shared_down_fmt: Optional[str] = None
     zipf_s: Optional[float] = None
     weight_sets: int = 1
     renormalize: bool = True
@@ -347,14 +350,15 @@ def make_layer(w: Workload, workers: Optional[int] = None) -> LayerWeights:
         note("gate")
         up = make_qweight(w.seed, "up", w.E, w.I, w.H, w.fmt, w.w_std, pool)
         note("up")
-        down = make_qweight(w.seed, "down", w.E, w.H, w.I, w.fmt, w.w_std, pool)
+        down = make_qweight(w.seed, "down", w.E, w.H, w.I, w.down_fmt or w.fmt, w.w_std, pool)
         note("down")
         sh = (None, None, None)
         if w.I_shared:
             sf = w.shared_fmt
             sh = (make_qweight(w.seed, "sh_gate", 1, w.I_shared, w.H, sf, w.w_std, pool),
                   make_qweight(w.seed, "sh_up", 1, w.I_shared, w.H, sf, w.w_std, pool),
-                  make_qweight(w.seed, "sh_down", 1, w.H, w.I_shared, sf, w.w_std, pool))
+                  make_qweight(w.seed, "sh_down", 1, w.H, w.I_shared, w.shared_down_fmt or sf,
+                               w.w_std, pool))
     finally:
         if pool is not None:
             pool.shutdown()

@@ -111,6 +111,34 @@ def test_layer_row_band(name):
         assert counts.max() > 16                 # a group takes more than one 16-row pass
 
 
+# Per-projection formats (the pages serve layers whose projections mix FP8 and
+# FP4): the down projections in another format than gate/up, routed and shared.
+MIXED = {
+    "nvfp4_gu_fp8_down": synth.scaled(W["tiny_nvfp4_t4"], name="mixed_nv_fp8", T=100, H=352,
+                                      E=12, I=160, top_k=3, fmt=synth.FMT_NVFP4,
+                                      down_fmt=synth.FMT_FP8, I_shared=96,
+                                      shared_fmt=synth.FMT_FP8,
+                                      shared_down_fmt=synth.FMT_NVFP4, zipf_s=1.1),
+    "mxfp4_gu_nvfp4_down": synth.scaled(W["tiny_nvfp4_t4"], name="mixed_mx_nv", T=100, H=512,
+                                        E=10, I=256, top_k=2, fmt=synth.FMT_MXFP4,
+                                        down_fmt=synth.FMT_NVFP4, I_shared=128,
+                                        shared_fmt=synth.FMT_MXFP4,
+                                        shared_down_fmt=synth.FMT_FP8),
+}
+
+
+@pytest.mark.parametrize("name", list(MIXED))
+@pytest.mark.parametrize("T", [1, 5, 12, 40, 100])
+def test_layer_mixed_formats(name, T):
+    """Fused decode (T <= 8), expert GEMV (T <= 64) and grouped GEMM (T = 100)."""
+    w = MIXED[name]
+    L = layer_for(w)
+    x_bits = synth.make_x(w)[:T]
+    say(f"[gpu] mixed formats {name} T={T}: gate/up {w.fmt}, down {w.down_fmt}, "
+        f"shared {w.shared_fmt}/{w.shared_down_fmt}")
+    check_layer_against_oracle(L, x_bits, what=f"{name} T={T}")
+
+
 @pytest.mark.parametrize("name", list(MID))
 def test_layer_grouped_gemm(name):
     w = MID[name]
