@@ -356,7 +356,7 @@ def dominant_kernel_name(w, mode="exact"):
         # K = H a multiple of 128: the LDS-DMA variant (whole K steps)
         base = "grouped_gemm_qd_kernel" if w.H % 128 == 0 else "grouped_gemm_q_kernel"
         return f"{base}<{ACT_MODES[mode][0]}, 0>"
-    fmt = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3}[w.fmt]
+    fmt = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3, "mxfp8": 4}[w.fmt]
     base = "expert_gemv_kernel" if w.T <= GEMV_MAX_ROWS else "grouped_gemm_kernel"
     return f"{base}<{fmt}, 0>"
 

@@ -61,11 +61,18 @@ extern "C" {
  * FP8_B128: codes uint8 E4M3 ("fn") [E][rows][cols]; scales fp32
  *   [E][ceil(rows/128)][ceil(cols/128)]; tensor_scale NULL.
  *   W[n,k] = e4m3(Q[n,k]) * S[n/128][k/128].  Requires cols % 16 == 0.
+ * MXFP8: codes uint8 E4M3 [E][rows][cols]; scales uint8 E8M0
+ *   [E][rows][cols/32]; tensor_scale NULL.  W[n,k] = e4m3(Q[n,k]) *
+ *   2^(S[n,k/32]-127) (OCP MX v1.0 MXFP8 E4M3).  Requires cols % 32 == 0.
+ *   The pages list MXFP8 among the checkpoint formats read as published
+ *   ("DGPP" README, intro bullet on checkpoint formats) and serve shared
+ *   experts in their shipped MXFP8 (README variant, supported-models table).
  * Element and scale encodings are those of the OCP Microscaling Formats v1.0
  * (E2M1, E8M0) and OCP 8-bit Floating Point (E4M3) specifications.         */
 #define MOE_FMT_NVFP4 1
 #define MOE_FMT_MXFP4 2
 #define MOE_FMT_FP8_B128 3
+#define MOE_FMT_MXFP8 4
 
 typedef struct moe_qweight {
   int32_t format;      /* MOE_FMT_* */

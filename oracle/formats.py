@@ -25,6 +25,11 @@ table):
   [ceil(rows/128)][ceil(cols/128)] (the checkpoint's 128x128 weight scales,
   gitee "dgpp" README, "Execution and performance", ``engine.prefill_fp8_gemm``).
   W[n,k] = e4m3(Q[n,k]) * S[n//128, k//128].
+* MXFP8 (OCP MX v1.0 E4M3 elements): codes uint8 E4M3 [rows][cols], E8M0
+  scale per 32 K, [rows][cols/32].  W[n,k] = e4m3(Q[n,k]) * e8m0(S[n,k//32]).
+  The pages list MXFP8 among the formats read as published ("DGPP" README,
+  intro bullet on checkpoint formats) and serve shared experts in it (README
+  variant, supported-models table).
 """
 from __future__ import annotations
 
@@ -90,6 +95,13 @@ def dequant_fp8_b128(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return q * s_full
 
 
+def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """One expert's MXFP8 matrix -> float64 [rows][cols]."""
+    q = e4m3_value(codes)
+    s = e8m0_value(scales)
+    return q * np.repeat(s, 32, axis=-1)
+
+
 def dequant(qw, expert: int) -> np.ndarray:
     """Decode expert `expert` of a stored projection (any format)."""
     if qw.fmt == "nvfp4":
@@ -98,4 +110,6 @@ def dequant(qw, expert: int) -> np.ndarray:
         return dequant_mxfp4(qw.codes[expert], qw.scales[expert])
     if qw.fmt == "fp8_b128":
         return dequant_fp8_b128(qw.codes[expert], qw.scales[expert])
+    if qw.fmt == "mxfp8":
+        return dequant_mxfp8(qw.codes[expert], qw.scales[expert])
     raise ValueError(f"unknown format {qw.fmt!r}")

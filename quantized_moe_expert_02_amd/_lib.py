@@ -23,6 +23,7 @@ MOE_ERR_HIP = -4
 MOE_FMT_NVFP4 = 1
 MOE_FMT_MXFP4 = 2
 MOE_FMT_FP8_B128 = 3
+MOE_FMT_MXFP8 = 4
 
 MOE_OP_GATE_UP_SWIGLU = 0
 MOE_OP_DOWN = 1

@@ -397,6 +397,7 @@ hipError_t by_shared_format(int sfmt, const DecodeArgs& a, hipStream_t s) {
     case FMT_NVFP4: return L::template run<RFMT, FMT_NVFP4>(a, s);
     case FMT_MXFP4: return L::template run<RFMT, FMT_MXFP4>(a, s);
     case FMT_FP8: return L::template run<RFMT, FMT_FP8>(a, s);
+    case FMT_MXFP8: return L::template run<RFMT, FMT_MXFP8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -407,6 +408,7 @@ hipError_t by_formats(int rfmt, int sfmt, const DecodeArgs& a, hipStream_t s) {
     case FMT_NVFP4: return by_shared_format<L, FMT_NVFP4>(sfmt, a, s);
     case FMT_MXFP4: return by_shared_format<L, FMT_MXFP4>(sfmt, a, s);
     case FMT_FP8: return by_shared_format<L, FMT_FP8>(sfmt, a, s);
+    case FMT_MXFP8: return by_shared_format<L, FMT_MXFP8>(sfmt, a, s);
     default: return hipErrorInvalidValue;
   }
 }

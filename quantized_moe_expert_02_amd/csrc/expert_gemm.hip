@@ -99,6 +99,9 @@ __device__ __forceinline__ void decode32(const Stage<FMT>& st, uint32_t (&w)[16]
       w[4 * d + 3] = c3.u;
     }
   } else {
+    // FP8: the block scale multiplies the 128-K partial; MXFP8: the E8M0 of
+    // the thread's 32-K block as the converter's scale (exact in bf16)
+    const float s = (FMT == FMT_MXFP8) ? __uint_as_float(st.s << 23) : 1.0f;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const uint32_t v = st.q[d / 4][d % 4];
@@ -106,8 +109,8 @@ __device__ __forceinline__ void decode32(const Stage<FMT>& st, uint32_t (&w)[16]
         bf16x2 h;
         uint32_t u;
       } c0, c1;
-      c0.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
-      c1.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true);
+      c0.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, false);
+      c1.h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, true);
       w[2 * d + 0] = c0.u;
       w[2 * d + 1] = c1.u;
     }
@@ -177,10 +180,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int kb = k0 + 32 * shalf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(arow + kb + 8 * i);
-    if constexpr (FMT == FMT_FP8) {
+    if constexpr (fmt_is_fp8(FMT)) {
       st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb);
       st.q[1] = *reinterpret_cast<const u32x4*>(wrow + kb + 16);
-      st.s = 0;
+      st.s = (FMT == FMT_MXFP8) ? wsrow[kb / 32] : 0u;
     } else {
       st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb / 2);
       st.q[1] = u32x4{0, 0, 0, 0};
@@ -203,7 +206,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     st.q[1] = u32x4{0, 0, 0, 0};
     st.s = 0;
     if (wvalid && kb < K) {
-      if constexpr (FMT == FMT_FP8) {
+      if constexpr (FMT == FMT_MXFP8) {  // K % 32 == 0: the 32-K block is whole
+        st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb);
+        st.q[1] = *reinterpret_cast<const u32x4*>(wrow + kb + 16);
+        st.s = wsrow[kb / 32];
+      } else if constexpr (FMT == FMT_FP8) {
         st.q[0] = *reinterpret_cast<const u32x4*>(wrow + kb);
         if (kb + 16 < K) st.q[1] = *reinterpret_cast<const u32x4*>(wrow + kb + 16);
       } else {
@@ -458,6 +465,7 @@ hipError_t launch_grouped_gemm(int op, const WDesc& w0, const WDesc& w1, const G
     case FMT_NVFP4: return launch_fmt<FMT_NVFP4>(op, p, nrt, s);
     case FMT_MXFP4: return launch_fmt<FMT_MXFP4>(op, p, nrt, s);
     case FMT_FP8: return launch_fmt<FMT_FP8>(op, p, nrt, s);
+    case FMT_MXFP8: return launch_fmt<FMT_MXFP8>(op, p, nrt, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -89,6 +89,7 @@ hipError_t launch_expert_gemv(int op, const WDesc& w0, const WDesc& w1, const Gr
     case FMT_NVFP4: return launch_fmt<FMT_NVFP4>(op, p, s);
     case FMT_MXFP4: return launch_fmt<FMT_MXFP4>(op, p, s);
     case FMT_FP8: return launch_fmt<FMT_FP8>(op, p, s);
+    case FMT_MXFP8: return launch_fmt<FMT_MXFP8>(op, p, s);
     default: return hipErrorInvalidValue;
   }
 }

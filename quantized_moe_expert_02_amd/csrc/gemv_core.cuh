@@ -52,10 +52,15 @@ struct ARaw<FMT_FP8> {
   u32x4 q0, q1;  // 32 E4M3 codes
   float s;       // the 128x128 block scale of this chunk
 };
+template <>
+struct ARaw<FMT_MXFP8> {
+  u32x4 q0, q1;  // 32 E4M3 codes: one MX block
+  uint32_t s;    // its E8M0 byte
+};
 
 template <int FMT>
 __device__ __forceinline__ int row_bytes(int K) {
-  return FMT == FMT_FP8 ? K : K / 2;
+  return fmt_is_fp8(FMT) ? K : K / 2;
 }
 
 // Load the lane's part of chunk c for weight row `row` (nullptr = zero row).
@@ -73,6 +78,15 @@ __device__ __forceinline__ ARaw<FMT> load_a(const uint8_t* __restrict__ row,
       if (k0 < K) a.q0 = *reinterpret_cast<const u32x4*>(row + k0);
       if (k0 + 16 < K) a.q1 = *reinterpret_cast<const u32x4*>(row + k0 + 16);
       a.s = reinterpret_cast<const float*>(srow)[c];
+    }
+  } else if constexpr (FMT == FMT_MXFP8) {
+    a.q0 = u32x4{0, 0, 0, 0};
+    a.q1 = u32x4{0, 0, 0, 0};
+    if constexpr (SC) a.s = 0;
+    if (row != nullptr && k0 < K) {  // K % 32 == 0: the block is whole
+      a.q0 = *reinterpret_cast<const u32x4*>(row + k0);
+      a.q1 = *reinterpret_cast<const u32x4*>(row + k0 + 16);
+      if constexpr (SC) a.s = srow[k0 / 32];
     }
   } else {
     a.q = u32x4{0, 0, 0, 0};
@@ -121,12 +135,16 @@ __device__ __forceinline__ bf16x8 decode_a(const ARaw<FMT>& a) {
     r.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 2);
     r.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 3);
   } else {
+    // FP8: the block scale multiplies the chunk's partial sum later; MXFP8:
+    // the E8M0 scale as the converter's scale (E4M3 x 2^e is exact in bf16)
+    float s = 1.0f;
+    if constexpr (FMT == FMT_MXFP8) s = __uint_as_float(a.s << 23);
     const uint32_t d0 = (I < 2) ? a.q0[2 * I] : a.q1[2 * I - 4];
     const uint32_t d1 = (I < 2) ? a.q0[2 * I + 1] : a.q1[2 * I - 3];
-    r.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
-    r.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
-    r.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
-    r.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+    r.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, s, false);
+    r.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, s, true);
+    r.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, s, false);
+    r.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, s, true);
   }
   return r.v;
 }
@@ -152,7 +170,7 @@ __device__ __forceinline__ const uint8_t* scale_row_ptr(const WDesc& w, int e, i
   if constexpr (FMT == FMT_NVFP4)
     return reinterpret_cast<const uint8_t*>(w.scales) + e * w.stride_scales +
            (size_t)n * (w.cols / 16);
-  else if constexpr (FMT == FMT_MXFP4)
+  else if constexpr (FMT == FMT_MXFP4 || FMT == FMT_MXFP8)
     return reinterpret_cast<const uint8_t*>(w.scales) + e * w.stride_scales +
            (size_t)n * (w.cols / 32);
   else  // FP8: the row of 128x128 block scales covering output row n

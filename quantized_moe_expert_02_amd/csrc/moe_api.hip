@@ -25,18 +25,21 @@ int fmt_of(int32_t f) {
     case MOE_FMT_NVFP4: return FMT_NVFP4;
     case MOE_FMT_MXFP4: return FMT_MXFP4;
     case MOE_FMT_FP8_B128: return FMT_FP8;
+    case MOE_FMT_MXFP8: return FMT_MXFP8;
     default: return 0;
   }
 }
 
 size_t codes_bytes(const moe_qweight& q) {
-  const size_t rb = (q.format == MOE_FMT_FP8_B128) ? (size_t)q.cols : (size_t)q.cols / 2;
+  const size_t rb = (q.format == MOE_FMT_FP8_B128 || q.format == MOE_FMT_MXFP8)
+                        ? (size_t)q.cols : (size_t)q.cols / 2;
   return rb * q.rows;
 }
 size_t scales_bytes(const moe_qweight& q) {
   switch (q.format) {
     case MOE_FMT_NVFP4: return (size_t)q.rows * (q.cols / 16);
-    case MOE_FMT_MXFP4: return (size_t)q.rows * (q.cols / 32);
+    case MOE_FMT_MXFP4:
+    case MOE_FMT_MXFP8: return (size_t)q.rows * (q.cols / 32);
     default: return (size_t)((q.rows + 127) / 128) * ((q.cols + 127) / 128) * 4;
   }
 }
@@ -74,7 +77,9 @@ WDesc wdesc(const moe_qweight& q) {
   w.stride_scales = q.expert_stride_scales;
   w.rows = q.rows;
   w.cols = q.cols;
-  const size_t word = (q.format == MOE_FMT_NVFP4) ? 8 : (q.format == MOE_FMT_MXFP4 ? 4 : 0);
+  const size_t word = (q.format == MOE_FMT_NVFP4)                                  ? 8
+                      : (q.format == MOE_FMT_MXFP4 || q.format == MOE_FMT_MXFP8) ? 4
+                                                                                 : 0;
   w.wide = word != 0 && q.cols % 128 == 0 && aligned(q.scales, word) &&
            (q.num_experts == 1 || q.expert_stride_scales % (int64_t)word == 0);
   return w;

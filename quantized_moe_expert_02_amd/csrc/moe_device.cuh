@@ -18,7 +18,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-enum : int { FMT_NVFP4 = 1, FMT_MXFP4 = 2, FMT_FP8 = 3 };
+enum : int { FMT_NVFP4 = 1, FMT_MXFP4 = 2, FMT_FP8 = 3, FMT_MXFP8 = 4 };
+
+// Formats whose codes are one byte per weight (E4M3).
+constexpr bool fmt_is_fp8(int f) { return f == FMT_FP8 || f == FMT_MXFP8; }
 
 // Activation modes of the expert GEMMs: the exact chain (bf16 inputs) and the
 // opt-in lossy ones (inputs quantized per row: MX E4M3 or E2M1 with an E8M0
@@ -35,9 +38,9 @@ struct WDesc {
   long long stride_codes;   // bytes between experts
   long long stride_scales;  // bytes between experts
   int rows, cols;
-  // FP4 only: cols % 128 == 0 and every scale row starts 8-byte (NVFP4) or
-  // 4-byte (MXFP4) aligned, so the block scales of a 128-wide K chunk of a
-  // row are one aligned word.
+  // NVFP4 / MXFP4 / MXFP8: cols % 128 == 0 and every scale row starts
+  // 8-byte (NVFP4) or 4-byte (MX) aligned, so the block scales of a 128-wide
+  // K chunk of a row are one aligned word.
   int wide;
 };
 

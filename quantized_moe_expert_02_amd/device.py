@@ -13,7 +13,8 @@ import torch
 
 from . import _lib
 
-_FMT = {"nvfp4": _lib.MOE_FMT_NVFP4, "mxfp4": _lib.MOE_FMT_MXFP4, "fp8_b128": _lib.MOE_FMT_FP8_B128}
+_FMT = {"nvfp4": _lib.MOE_FMT_NVFP4, "mxfp4": _lib.MOE_FMT_MXFP4, "fp8_b128": _lib.MOE_FMT_FP8_B128,
+        "mxfp8": _lib.MOE_FMT_MXFP8}
 
 
 class DeviceLayer:

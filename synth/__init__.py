@@ -25,6 +25,8 @@ Encoders (generator side only):
   X = floor(log2(amax_b)) - 2, q = RNE_e2m1(w/2^X) saturated to +-6.
 * FP8 E4M3 ("fn", no infinities) with one fp32 scale per 128x128 block:
   s = amax_blk/448, q = RNE_e4m3(w/s).
+* MXFP8 (OCP MX v1.0, E4M3 elements): E8M0 scale 2^X per 32 elements with
+  X = floor(log2(amax_b)) - 8, q = RNE_e4m3(w/2^X) saturated to +-448.
 """
 from __future__ import annotations
 
@@ -41,7 +43,8 @@ GENERATOR_VERSION = 1
 FMT_NVFP4 = "nvfp4"
 FMT_MXFP4 = "mxfp4"
 FMT_FP8 = "fp8_b128"
-FORMATS = (FMT_NVFP4, FMT_MXFP4, FMT_FP8)
+FMT_MXFP8 = "mxfp8"
+FORMATS = (FMT_NVFP4, FMT_MXFP4, FMT_FP8, FMT_MXFP8)
 
 # Sub-seed identifiers: every tensor draws from SeedSequence(seed, (id, expert)).
 _TID = {"x": 1, "router": 2, "zipf_perm": 3, "gate": 4, "up": 5, "down": 6,
@@ -300,6 +303,19 @@ def encode_fp8_b128(w: np.ndarray):
     return q, s
 
 
+def encode_mxfp8(w: np.ndarray):
+    rows, cols = w.shape
+    assert cols % 32 == 0
+    w = w.astype(np.float64)
+    blk = w.reshape(rows, cols // 32, 32)
+    amax_b = np.max(np.abs(blk), axis=2)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax_b > 0, np.floor(np.log2(np.where(amax_b > 0, amax_b, 1.0))) - 8, -127)
+    X = np.clip(X, -127, 127)
+    q = blk / np.exp2(X)[..., None]
+    return enc_e4m3(q).reshape(rows, cols), (X + 127).astype(np.uint8)
+
+
 def _gen_matrix(args):
     seed, tensor, expert, rows, cols, fmt, std = args
     g = _rng(seed, tensor, expert)
@@ -312,6 +328,9 @@ def _gen_matrix(args):
         return c, s, None
     if fmt == FMT_FP8:
         c, s = encode_fp8_b128(w)
+        return c, s, None
+    if fmt == FMT_MXFP8:
+        c, s = encode_mxfp8(w)
         return c, s, None
     raise ValueError(fmt)
 

@@ -127,6 +127,30 @@ MIXED = {
 }
 
 
+# MXFP8 experts (E4M3 codes, E8M0 per 32): routed with ragged and with
+# 128-aligned K, and as the shared expert beside NVFP4 routed experts.
+MXFP8 = {
+    "mxfp8_ragged": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp8_ragged", T=150, H=352, E=12,
+                                 I=160, top_k=3, fmt=synth.FMT_MXFP8, I_shared=96,
+                                 shared_fmt=synth.FMT_MXFP8, zipf_s=1.1),
+    "mxfp8_aligned": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp8_aligned", T=150, H=512, E=10,
+                                  I=256, top_k=2, fmt=synth.FMT_MXFP8, I_shared=128,
+                                  shared_fmt=synth.FMT_FP8),
+    "nvfp4_mxfp8_shared": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_mxfp8_shared", T=150,
+                                       H=512, E=10, I=256, top_k=2, fmt=synth.FMT_NVFP4,
+                                       I_shared=128, shared_fmt=synth.FMT_MXFP8),
+}
+
+
+@pytest.mark.parametrize("name", list(MXFP8))
+@pytest.mark.parametrize("T", [1, 5, 40, 150])
+def test_layer_mxfp8(name, T):
+    """Fused decode (T <= 8), expert GEMV (T = 40) and grouped GEMM (T = 150)."""
+    w = MXFP8[name]
+    say(f"[gpu] MXFP8 layer {name} T={T}")
+    check_layer_against_oracle(layer_for(w), synth.make_x(w)[:T], what=f"{name} T={T}")
+
+
 @pytest.mark.parametrize("name", list(MIXED))
 @pytest.mark.parametrize("T", [1, 5, 12, 40, 100])
 def test_layer_mixed_formats(name, T):

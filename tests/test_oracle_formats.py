@@ -93,6 +93,22 @@ def test_mxfp4_hand_worked_block():
     assert np.all(np.isnan(w[1, 32:]))
 
 
+def test_mxfp8_hand_worked_block():
+    codes = np.zeros((2, 64), np.uint8)
+    codes[0, :32] = 0x38        # 1.0
+    codes[0, 32:] = 0xC0        # -2.0
+    codes[1, :32] = 0x7E        # 448
+    codes[1, 40] = 0x7F         # NaN code
+    codes[1, 33] = 0x01         # smallest subnormal, 2^-9
+    scales = np.array([[127 + 3, 127 - 2], [127, 127 + 1]], np.uint8)
+    w = F.dequant_mxfp8(codes, scales)
+    assert np.all(w[0, :32] == 8.0) and np.all(w[0, 32:] == -0.5)
+    assert np.all(w[1, :32] == 448.0) and np.isnan(w[1, 40])
+    assert w[1, 33] == 2.0 ** -8 and w[1, 34] == 0.0
+    scales[0, 0] = 0xFF
+    assert np.all(np.isnan(F.dequant_mxfp8(codes, scales)[0, :32]))
+
+
 def test_fp8_b128_edge_blocks():
     rows, cols = 130, 200
     codes = np.full((rows, cols), 0x38, np.uint8)      # 1.0 everywhere
@@ -117,6 +133,13 @@ def test_round_trip_through_generator_encoders(fmt):
         # E4M3 keeps 4 significant bits: rel. error <= 2^-4 (plus subnormal quantum)
         s = np.repeat(np.repeat(qw.scales[0], 128, 0), 128, 1)[:256, :384]
         assert np.all(np.abs(d - w) <= np.abs(w) * 2.0 ** -4 + s * 2.0 ** -10)
+    elif fmt == synth.FMT_MXFP8:
+        # E4M3 rounding plus saturation: the OCP shared exponent leaves
+        # |w|/s in [256, 512) for the block maximum, clamped to 448
+        s = np.repeat(F.e8m0_value(qw.scales[0]), 32, axis=1)
+        sat = np.maximum(0.0, np.abs(w) - 448.0 * s)
+        assert np.all(np.abs(d - w) <= np.abs(w) * 2.0 ** -4 + s * 2.0 ** -10 + sat + 1e-15)
+        assert np.all(sat <= np.abs(w) / 8)
     else:
         blk = 16 if fmt == synth.FMT_NVFP4 else 32
         if fmt == synth.FMT_NVFP4:
@@ -143,6 +166,9 @@ def _encode(fmt, w):
         return c[None], s[None], np.array([ts], np.float32)
     if fmt == synth.FMT_MXFP4:
         c, s = synth.encode_mxfp4(w)
+        return c[None], s[None], None
+    if fmt == synth.FMT_MXFP8:
+        c, s = synth.encode_mxfp8(w)
         return c[None], s[None], None
     c, s = synth.encode_fp8_b128(w)
     return c[None], s[None], None
