@@ -141,7 +141,8 @@ int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits
  * (pairs in t-major, slot order within each expert).
  *   topk_ids int32 [T][k] with values in [0, E) (out-of-range ids are dropped).
  *   counts [E]; offsets [E+1] (exclusive scan of counts);
- *   perm_to_pair [T*k]: permuted row -> pair t*k+j; pair_to_perm [T*k]: inverse.
+ *   perm_to_pair [T*k]: permuted row -> pair t*k+j (the first offsets[E]
+ *            entries); pair_to_perm [T*k]: inverse, -1 for a dropped pair.
  *   active_experts int32 [E+1] or NULL: element 0 = number of experts with at
  *            least one row, then their ids in increasing order.
  * Workspace: moe_permute_workspace_size(T, k, E) bytes. */
@@ -177,7 +178,8 @@ int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
 /* Weighted combine (partials kept in fp32, summed in slot order; bf16
  * partials are a lossy lever on the pages, gitee "dgpp" README, "Execution
  * and performance", engine.prefill_bf16_partials):
- *   out[t] = bf16( sum_{j<k} w[t,j] * y_perm[pair_to_perm[t*k+j]] + y_shared[t] ).
+ *   out[t] = bf16( sum_{j<k} w[t,j] * y_perm[pair_to_perm[t*k+j]] + y_shared[t] ),
+ *   a pair with pair_to_perm -1 (dropped by the grouping) contributing nothing.
  *   y_perm fp32 [T*k][H]; topk_w fp32 [T][k]; y_shared fp32 [T][H] or NULL;
  *   out bf16 [T][H]. */
 int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pair_to_perm,
@@ -261,6 +263,36 @@ int32_t moe_expert_gemm_q(int32_t mode, int32_t op, const moe_layer_desc* L, int
 int32_t moe_layer_forward_ex(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
                              void* ws, size_t ws_bytes, int32_t act_mode, float* dbg_logits,
                              int32_t* dbg_ids, float* dbg_w, void* stream);
+
+/* ---- routing from a token table, and the layer on a given routing --------
+ * The pages route the first layers of one served model by a token table
+ * ("DGPP" README variant, supported-models notes on DeepSeek-V4-Flash;
+ * source layout, the dsv4 model directory) and give no more detail.  The
+ * reading taken: the experts of token t are row token_ids[t] of `table`, in
+ * table order, and the weights are the layer's own router function at those
+ * experts (the softmax over the k selected logits, or with renormalize == 0
+ * the full softmax gathered).
+ *   token_ids int32 [T]; table int32 [V][k] (k = L->top_k).
+ *   x bf16 [T][H] or NULL; logits fp32 [T][E]: with x NULL the input, else
+ *     the router's logits are written there (NULL: kept in the workspace).
+ *   topk_ids int32 [T][k], topk_w fp32 [T][k] (weights computed in float64).
+ * A token id outside [0, V) selects nothing (ids -1, weights 0); a table
+ * entry outside [0, E) is passed through with weight 0 and no part in the
+ * normalisation (the grouping drops it).  NaN logits: unspecified.
+ * Workspace: moe_workspace_size(L, T). */
+int32_t moe_route_table(const moe_layer_desc* L, const uint16_t* x, float* logits,
+                        const int32_t* token_ids, const int32_t* table, int32_t V, int32_t T,
+                        int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* moe_layer_forward_ex on a given routing (topk_ids int32 [T][k], topk_w fp32
+ * [T][k], device, e.g. from moe_route_topk or moe_route_table) instead of the
+ * router: grouping, experts, shared expert and combine.  Expert ids outside
+ * [0, E) are dropped (their slots contribute nothing).  For T <= 8 only the
+ * fused decode's two expert launches run. */
+int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int32_t T,
+                                 const int32_t* topk_ids, const float* topk_w, uint16_t* out,
+                                 void* ws, size_t ws_bytes, int32_t act_mode, void* stream);
 
 #ifdef __cplusplus
 }

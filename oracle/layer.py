@@ -196,6 +196,41 @@ def route_from_logits(logits: np.ndarray, k: int, renormalize: bool = True):
     return ids, wts
 
 
+def route_from_table(token_ids, table, logits, renormalize: bool = True):
+    """Token-table routing: the experts of token t are row token_ids[t] of
+    `table` [V][k], in table order; the weights are the layer's softmax (over
+    the k selected logits, or the full softmax gathered) at those experts.
+    The pages route the first layers of one served model by a token table
+    and say no more; this is the plain reading (expert choice from the
+    table, weighting by the layer's own router function).  A token id outside
+    [0, V) selects nothing (ids -1, weights 0); a table entry outside [0, E)
+    gets weight 0 and takes no part in the normalisation."""
+    token_ids = np.asarray(token_ids, dtype=np.int64)
+    table = np.asarray(table, dtype=np.int64)
+    l = np.asarray(logits, dtype=np.float64)
+    T, E = l.shape
+    V, k = table.shape
+    ids = np.full((T, k), -1, dtype=np.int32)
+    wts = np.zeros((T, k))
+    for t in range(T):
+        if not 0 <= token_ids[t] < V:
+            continue
+        row = table[token_ids[t]]
+        ids[t] = row
+        ok = (row >= 0) & (row < E)
+        if not ok.any():
+            continue
+        sel = l[t, row[ok]]
+        with np.errstate(invalid="ignore", over="ignore"):
+            if renormalize:
+                z = np.exp(sel - np.max(sel))
+                wts[t, ok] = z / np.sum(z)
+            else:
+                m = np.max(l[t])
+                wts[t, ok] = np.exp(sel - m) / np.sum(np.exp(l[t] - m))
+    return ids, wts
+
+
 # ---------------------------------------------------------------------------
 # grouping
 # ---------------------------------------------------------------------------
@@ -208,13 +243,18 @@ class Grouping:
 
 
 def permute(ids: np.ndarray, E: int) -> Grouping:
-    """Stable counting sort of the pairs (t, j), t-major, keyed by expert id."""
+    """Stable counting sort of the pairs (t, j), t-major, keyed by expert id.
+    Pairs whose id is outside [0, E) are dropped: they follow the sorted pairs
+    in perm_to_pair and have pair_to_perm -1."""
     flat = np.asarray(ids, dtype=np.int64).reshape(-1)
-    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int32)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    p2pair = np.argsort(flat, kind="stable").astype(np.int32)
+    key = np.where(valid, flat, E)
+    p2pair = np.argsort(key, kind="stable").astype(np.int32)
     pair2p = np.empty_like(p2pair)
     pair2p[p2pair] = np.arange(flat.size, dtype=np.int32)
+    pair2p[~valid] = -1
     return Grouping(counts, offsets, p2pair, pair2p)
 
 
@@ -289,6 +329,8 @@ def layer_forward(L, x_bits: np.ndarray, tokens=None, routing: Optional[Routing]
     y = np.zeros((n, k, L.H))
     sel = R.ids[toks]
     for e in np.unique(sel):
+        if not 0 <= e < L.E:  # a dropped pair: no FFN, y stays 0
+            continue
         rows, slots = np.nonzero(sel == e)
         he = ffn_gate_up(x64[rows], dec("gate", int(e)), dec("up", int(e)))
         h[rows, slots] = he

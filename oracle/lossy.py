@@ -200,6 +200,8 @@ def layer_forward(L, x_bits: np.ndarray, mode: Optional[str], tokens=None,
     y = np.zeros((n, k, L.H))
     sel = R.ids[toks]
     for e in np.unique(sel):
+        if not 0 <= e < L.E:  # a dropped pair: no FFN, y stays 0
+            continue
         rows, slots = np.nonzero(sel == e)
         he, ye = ffn(x64[rows], dec("gate", int(e)), dec("up", int(e)), dec("down", int(e)),
                      L.gate.fmt, L.down.fmt, mode)

@@ -36,7 +36,7 @@ MOE_ACT_FP8_T128 = 3
 EXPORTED = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_validate_layer", "moe_workspace_size",
             "moe_route_topk", "moe_permute_workspace_size", "moe_permute", "moe_expert_gemm",
             "moe_combine", "moe_layer_forward", "moe_quantize_act", "moe_expert_gemm_q",
-            "moe_layer_forward_ex"]
+            "moe_layer_forward_ex", "moe_route_table", "moe_layer_forward_routed"]
 
 
 class MoeError(RuntimeError):
@@ -88,6 +88,8 @@ def _load():
         "moe_quantize_act": (I32, [I32, P, I32, I32, P, P, P]),
         "moe_expert_gemm_q": (I32, [I32, I32, LP, I32, P, P, P, I32, P, P, P, P, SZ, P]),
         "moe_layer_forward_ex": (I32, [LP, P, I32, P, P, SZ, I32, P, P, P, P]),
+        "moe_route_table": (I32, [LP, P, P, P, P, I32, I32, P, P, P, SZ, P]),
+        "moe_layer_forward_routed": (I32, [LP, P, I32, P, P, P, P, SZ, I32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -200,3 +202,19 @@ def moe_expert_gemm_q(mode, op, L, shared, offsets, perm_to_pair, active_experts
                                _p(active_experts), T, _p(in_codes), _p(in_scales), _p(out), _p(ws),
                                wsb, _stream(stream))
     return _check(st, "moe_expert_gemm_q") if check else st
+
+
+def moe_route_table(L, x, logits, token_ids, table, V, T, topk_ids, topk_w, ws, ws_bytes=None,
+                    stream=None, check=True):
+    wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    st = LIB.moe_route_table(ctypes.byref(L), _p(x), _p(logits), _p(token_ids), _p(table), V, T,
+                             _p(topk_ids), _p(topk_w), _p(ws), wsb, _stream(stream))
+    return _check(st, "moe_route_table") if check else st
+
+
+def moe_layer_forward_routed(L, x, T, topk_ids, topk_w, out, ws, act_mode=0, ws_bytes=None,
+                             stream=None, check=True):
+    wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    st = LIB.moe_layer_forward_routed(ctypes.byref(L), _p(x), T, _p(topk_ids), _p(topk_w), _p(out),
+                                      _p(ws), wsb, act_mode, _stream(stream))
+    return _check(st, "moe_layer_forward_routed") if check else st

@@ -30,7 +30,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const int j = min(j0 + b, k - 1);  // in bounds; slots past k are not summed
       const int pp = p2p[(size_t)t * k + j];
       wj[b] = w[(size_t)t * k + j];
-      v[b] = *reinterpret_cast<const f32x4*>(y + (size_t)pp * H + n);
+      // a dropped pair (pair_to_perm -1) contributes nothing
+      v[b] = (pp >= 0) ? *reinterpret_cast<const f32x4*>(y + (size_t)pp * H + n)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (pp < 0) wj[b] = 0.f;
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {

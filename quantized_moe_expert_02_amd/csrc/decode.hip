@@ -431,6 +431,12 @@ hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s) {
   return launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
 }
 
+hipError_t launch_decode_experts(const DecodeArgs& a, hipStream_t s) {
+  hipError_t err = by_formats<GateUpLaunch>(a.gate.fmt, a.has_shared ? a.sg.fmt : 0, a, s);
+  if (err != hipSuccess) return err;
+  return by_formats<DownLaunch>(a.down.fmt, a.has_shared ? a.sd.fmt : 0, a, s);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   hipError_t err = launch(decode_router_kernel, dim3(a.RS * a.CS), dim3(256), 0, s, a);
   if (err != hipSuccess) return err;

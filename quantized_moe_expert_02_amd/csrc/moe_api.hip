@@ -139,6 +139,7 @@ struct WsPlan {
   // lossy activation modes (T > kGemvMaxRows): quantized x, h and shared h
   // (codes sized for E4M3, scales 4 bytes per 128 K per row)
   size_t xq, xqs, hq, hqs, hsq, hsqs;
+  size_t tlog;
 };
 
 constexpr int kDecodeRows = 8;
@@ -199,6 +200,7 @@ WsPlan plan(const moe_layer_desc* L, int T) {
     p.dpart = take((size_t)p.dp.RS * T * E * 4);
     p.dapart = take((size_t)p.dp.RS * T * E * 4);
   }
+  p.tlog = take((size_t)T * E * 4);  // router logits for token-table routing
   p.xq = p.xqs = p.hq = p.hqs = p.hsq = p.hsqs = 0;
   if (T > kGemvMaxRows) {
     auto sb = [](int K) { return (size_t)act_scale_pitch(K); };
@@ -380,6 +382,137 @@ int32_t run_experts_q(int32_t mode, int op, const moe_layer_desc* L, int shared,
                                           max_tiles, codes, scales, out, s));
 }
 
+// The layer.  given_ids / given_w: a routing to use instead of the router
+// (moe_layer_forward_routed), else nullptr.
+int32_t layer_impl(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out, void* ws,
+                   size_t ws_bytes, int32_t act_mode, float* dbg_logits, int32_t* dbg_ids,
+                   float* dbg_w, const int32_t* given_ids, const float* given_w, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (act_mode != MOE_ACT_EXACT) {
+    if (!act_mode_valid(act_mode)) return MOE_ERR_INVALID_ARG;
+    const bool any = mode_applies(act_mode, L->gate.format) ||
+                     mode_applies(act_mode, L->down.format) ||
+                     (L->has_shared && (mode_applies(act_mode, L->sh_gate.format) ||
+                                        mode_applies(act_mode, L->sh_down.format)));
+    if (!any) return MOE_ERR_UNSUPPORTED;
+    // the quantizer works on whole 32-element blocks of K
+    auto k_ok = [&](const moe_qweight& q) {
+      return !mode_applies(act_mode, q.format) || q.cols % 32 == 0;
+    };
+    if (!k_ok(L->gate) || !k_ok(L->down) ||
+        (L->has_shared && (!k_ok(L->sh_gate) || !k_ok(L->sh_down))))
+      return MOE_ERR_UNSUPPORTED;
+  }
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || out == nullptr || !aligned(x, 16) || !aligned(out, 16))
+    return MOE_ERR_INVALID_ARG;
+  const WsPlan p = plan(L, T);
+  if (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool routed = given_ids != nullptr;
+  // (the kernels only read a given routing)
+  int* ids = routed ? const_cast<int*>(given_ids) : (dbg_ids ? dbg_ids : at<int>(ws, p.ids));
+  float* w = routed ? const_cast<float*>(given_w) : (dbg_w ? dbg_w : at<float>(ws, p.w));
+  if (T <= kDecodeRows) {
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.T = T;
+    a.H = L->H;
+    a.I = L->I;
+    a.E = L->E;
+    a.k = L->top_k;
+    a.renorm = L->renormalize;
+    a.I_shared = L->has_shared ? L->I_shared : 0;
+    a.has_shared = L->has_shared;
+    a.max_groups = p.P < L->E ? p.P : L->E;
+    a.wr = L->router_w;
+    a.bias = L->router_bias;
+    a.gate = wdesc(L->gate);
+    a.up = wdesc(L->up);
+    a.down = wdesc(L->down);
+    if (L->has_shared) {
+      a.sg = wdesc(L->sh_gate);
+      a.su = wdesc(L->sh_up);
+      a.sd = wdesc(L->sh_down);
+    }
+    a.RS = p.dp.RS;
+    a.CS = p.dp.CS;
+    a.part = at<float>(ws, p.dpart);
+    a.apart = at<float>(ws, p.dapart);
+    a.logits_out = dbg_logits;
+    a.ids = ids;
+    a.w = w;
+    a.h = at<uint16_t>(ws, p.h);
+    a.hs = L->has_shared ? at<uint16_t>(ws, p.hs) : nullptr;
+    a.out = out;
+    return hip_status(routed ? launch_decode_experts(a, s) : launch_decode(a, s));
+  }
+  if (!routed && (st = run_route(L, x, dbg_logits, T, ids, w, ws, p, s)) != MOE_OK) return st;
+  int* offsets = at<int>(ws, p.offsets);
+  int* p2pair = at<int>(ws, p.p2pair);
+  int* pair2p = at<int>(ws, p.pair2p);
+  if ((st = hip_status(launch_permute(ids, T, L->top_k, L->E, at<int>(ws, p.counts), offsets,
+                                      p2pair, pair2p, at<int>(ws, p.hist), at<int>(ws, p.act),
+                                      at<int>(ws, p.nact), p.tile_m, at<int>(ws, p.tiles),
+                                      at<int>(ws, p.ntiles), p.max_tiles, s))) != MOE_OK)
+    return st;
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  float* y = at<float>(ws, p.y);
+  const int* active = at<int>(ws, p.nact);
+  // Lossy modes (prefill lowering only): which projections quantize their inputs.
+  const bool lossy = act_mode != MOE_ACT_EXACT && T > kGemvMaxRows;
+  const bool q_gu = lossy && mode_applies(act_mode, L->gate.format);
+  const bool q_d = lossy && mode_applies(act_mode, L->down.format);
+  const bool q_sgu = lossy && L->has_shared && mode_applies(act_mode, L->sh_gate.format);
+  const bool q_sd = lossy && L->has_shared && mode_applies(act_mode, L->sh_down.format);
+  const int km = act_kernel_mode(act_mode);
+  uint8_t* xq = at<uint8_t>(ws, p.xq);
+  void* xqs = at<void>(ws, p.xqs);
+  if ((q_gu || q_sgu) &&
+      (st = hip_status(launch_quantize_act(km, x, T, L->H, xq, xqs, s))) != MOE_OK)
+    return st;
+  st = q_gu ? run_experts_q(act_mode, MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, xq,
+                            xqs, h, ws, p, true, s)
+            : run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, x, h, ws, p,
+                          true, s);
+  if (st != MOE_OK) return st;
+  if (q_d) {
+    uint8_t* hq = at<uint8_t>(ws, p.hq);
+    void* hqs = at<void>(ws, p.hqs);
+    if ((st = hip_status(launch_quantize_act(km, h, p.P, L->I, hq, hqs, s))) != MOE_OK) return st;
+    st = run_experts_q(act_mode, MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, hq, hqs, y, ws, p,
+                       true, s);
+  } else {
+    st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, h, y, ws, p, true, s);
+  }
+  if (st != MOE_OK) return st;
+  float* ys = nullptr;
+  if (L->has_shared) {
+    uint16_t* hs = at<uint16_t>(ws, p.hs);
+    ys = at<float>(ws, p.ys);
+    st = q_sgu ? run_experts_q(act_mode, MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T,
+                               xq, xqs, hs, ws, p, true, s)
+               : run_experts(MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T, x, hs, ws,
+                             p, true, s);
+    if (st != MOE_OK) return st;
+    if (q_sd) {
+      uint8_t* hsq = at<uint8_t>(ws, p.hsq);
+      void* hsqs = at<void>(ws, p.hsqs);
+      if ((st = hip_status(launch_quantize_act(km, hs, T, L->I_shared, hsq, hsqs, s))) != MOE_OK)
+        return st;
+      st = run_experts_q(act_mode, MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hsq, hsqs, ys,
+                         ws, p, true, s);
+    } else {
+      st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hs, ys, ws, p, true, s);
+    }
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(launch_combine(y, w, pair2p, ys, T, L->top_k, L->H, out, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -482,135 +615,54 @@ int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pai
 int32_t moe_layer_forward_ex(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
                              void* ws, size_t ws_bytes, int32_t act_mode, float* dbg_logits,
                              int32_t* dbg_ids, float* dbg_w, void* stream) {
-  int32_t st = check_layer(L);
-  if (st != MOE_OK) return st;
-  if (act_mode != MOE_ACT_EXACT) {
-    if (!act_mode_valid(act_mode)) return MOE_ERR_INVALID_ARG;
-    const bool any = mode_applies(act_mode, L->gate.format) ||
-                     mode_applies(act_mode, L->down.format) ||
-                     (L->has_shared && (mode_applies(act_mode, L->sh_gate.format) ||
-                                        mode_applies(act_mode, L->sh_down.format)));
-    if (!any) return MOE_ERR_UNSUPPORTED;
-    // the quantizer works on whole 32-element blocks of K
-    auto k_ok = [&](const moe_qweight& q) {
-      return !mode_applies(act_mode, q.format) || q.cols % 32 == 0;
-    };
-    if (!k_ok(L->gate) || !k_ok(L->down) ||
-        (L->has_shared && (!k_ok(L->sh_gate) || !k_ok(L->sh_down))))
-      return MOE_ERR_UNSUPPORTED;
-  }
-  if (T < 0) return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
-  if (x == nullptr || out == nullptr || !aligned(x, 16) || !aligned(out, 16))
-    return MOE_ERR_INVALID_ARG;
-  const WsPlan p = plan(L, T);
-  if (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)) return MOE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int* ids = dbg_ids ? dbg_ids : at<int>(ws, p.ids);
-  float* w = dbg_w ? dbg_w : at<float>(ws, p.w);
-  if (T <= kDecodeRows) {
-    DecodeArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.x = x;
-    a.T = T;
-    a.H = L->H;
-    a.I = L->I;
-    a.E = L->E;
-    a.k = L->top_k;
-    a.renorm = L->renormalize;
-    a.I_shared = L->has_shared ? L->I_shared : 0;
-    a.has_shared = L->has_shared;
-    a.max_groups = p.P < L->E ? p.P : L->E;
-    a.wr = L->router_w;
-    a.bias = L->router_bias;
-    a.gate = wdesc(L->gate);
-    a.up = wdesc(L->up);
-    a.down = wdesc(L->down);
-    if (L->has_shared) {
-      a.sg = wdesc(L->sh_gate);
-      a.su = wdesc(L->sh_up);
-      a.sd = wdesc(L->sh_down);
-    }
-    a.RS = p.dp.RS;
-    a.CS = p.dp.CS;
-    a.part = at<float>(ws, p.dpart);
-    a.apart = at<float>(ws, p.dapart);
-    a.logits_out = dbg_logits;
-    a.ids = ids;
-    a.w = w;
-    a.h = at<uint16_t>(ws, p.h);
-    a.hs = L->has_shared ? at<uint16_t>(ws, p.hs) : nullptr;
-    a.out = out;
-    return hip_status(launch_decode(a, s));
-  }
-  if ((st = run_route(L, x, dbg_logits, T, ids, w, ws, p, s)) != MOE_OK) return st;
-  int* offsets = at<int>(ws, p.offsets);
-  int* p2pair = at<int>(ws, p.p2pair);
-  int* pair2p = at<int>(ws, p.pair2p);
-  if ((st = hip_status(launch_permute(ids, T, L->top_k, L->E, at<int>(ws, p.counts), offsets,
-                                      p2pair, pair2p, at<int>(ws, p.hist), at<int>(ws, p.act),
-                                      at<int>(ws, p.nact), p.tile_m, at<int>(ws, p.tiles),
-                                      at<int>(ws, p.ntiles), p.max_tiles, s))) != MOE_OK)
-    return st;
-  uint16_t* h = at<uint16_t>(ws, p.h);
-  float* y = at<float>(ws, p.y);
-  const int* active = at<int>(ws, p.nact);
-  // Lossy modes (prefill lowering only): which projections quantize their inputs.
-  const bool lossy = act_mode != MOE_ACT_EXACT && T > kGemvMaxRows;
-  const bool q_gu = lossy && mode_applies(act_mode, L->gate.format);
-  const bool q_d = lossy && mode_applies(act_mode, L->down.format);
-  const bool q_sgu = lossy && L->has_shared && mode_applies(act_mode, L->sh_gate.format);
-  const bool q_sd = lossy && L->has_shared && mode_applies(act_mode, L->sh_down.format);
-  const int km = act_kernel_mode(act_mode);
-  uint8_t* xq = at<uint8_t>(ws, p.xq);
-  void* xqs = at<void>(ws, p.xqs);
-  if ((q_gu || q_sgu) &&
-      (st = hip_status(launch_quantize_act(km, x, T, L->H, xq, xqs, s))) != MOE_OK)
-    return st;
-  st = q_gu ? run_experts_q(act_mode, MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, xq,
-                            xqs, h, ws, p, true, s)
-            : run_experts(MOE_OP_GATE_UP_SWIGLU, L, 0, offsets, p2pair, active, T, x, h, ws, p,
-                          true, s);
-  if (st != MOE_OK) return st;
-  if (q_d) {
-    uint8_t* hq = at<uint8_t>(ws, p.hq);
-    void* hqs = at<void>(ws, p.hqs);
-    if ((st = hip_status(launch_quantize_act(km, h, p.P, L->I, hq, hqs, s))) != MOE_OK) return st;
-    st = run_experts_q(act_mode, MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, hq, hqs, y, ws, p,
-                       true, s);
-  } else {
-    st = run_experts(MOE_OP_DOWN, L, 0, offsets, p2pair, active, T, h, y, ws, p, true, s);
-  }
-  if (st != MOE_OK) return st;
-  float* ys = nullptr;
-  if (L->has_shared) {
-    uint16_t* hs = at<uint16_t>(ws, p.hs);
-    ys = at<float>(ws, p.ys);
-    st = q_sgu ? run_experts_q(act_mode, MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T,
-                               xq, xqs, hs, ws, p, true, s)
-               : run_experts(MOE_OP_GATE_UP_SWIGLU, L, 1, nullptr, nullptr, nullptr, T, x, hs, ws,
-                             p, true, s);
-    if (st != MOE_OK) return st;
-    if (q_sd) {
-      uint8_t* hsq = at<uint8_t>(ws, p.hsq);
-      void* hsqs = at<void>(ws, p.hsqs);
-      if ((st = hip_status(launch_quantize_act(km, hs, T, L->I_shared, hsq, hsqs, s))) != MOE_OK)
-        return st;
-      st = run_experts_q(act_mode, MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hsq, hsqs, ys,
-                         ws, p, true, s);
-    } else {
-      st = run_experts(MOE_OP_DOWN, L, 1, nullptr, nullptr, nullptr, T, hs, ys, ws, p, true, s);
-    }
-    if (st != MOE_OK) return st;
-  }
-  return hip_status(launch_combine(y, w, pair2p, ys, T, L->top_k, L->H, out, s));
+  return layer_impl(L, x, T, out, ws, ws_bytes, act_mode, dbg_logits, dbg_ids, dbg_w, nullptr,
+                    nullptr, stream);
 }
 
 int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
                           void* ws, size_t ws_bytes, float* dbg_logits, int32_t* dbg_ids,
                           float* dbg_w, void* stream) {
-  return moe_layer_forward_ex(L, x, T, out, ws, ws_bytes, MOE_ACT_EXACT, dbg_logits, dbg_ids,
-                              dbg_w, stream);
+  return layer_impl(L, x, T, out, ws, ws_bytes, MOE_ACT_EXACT, dbg_logits, dbg_ids, dbg_w, nullptr,
+                    nullptr, stream);
+}
+
+int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int32_t T,
+                                 const int32_t* topk_ids, const float* topk_w, uint16_t* out,
+                                 void* ws, size_t ws_bytes, int32_t act_mode, void* stream) {
+  if (T <= 0)  // checks of L and T only; nothing runs
+    return layer_impl(L, x, T, out, ws, ws_bytes, act_mode, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, stream);
+  if (topk_ids == nullptr || topk_w == nullptr || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
+  return layer_impl(L, x, T, out, ws, ws_bytes, act_mode, nullptr, nullptr, nullptr, topk_ids,
+                    topk_w, stream);
+}
+
+int32_t moe_route_table(const moe_layer_desc* L, const uint16_t* x, float* logits,
+                        const int32_t* token_ids, const int32_t* table, int32_t V, int32_t T,
+                        int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int32_t st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0 || V <= 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (token_ids == nullptr || table == nullptr || topk_ids == nullptr || topk_w == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (x == nullptr && logits == nullptr) return MOE_ERR_INVALID_ARG;
+  if (x != nullptr && (!aligned(x, 16) || L->H % 8 != 0)) return MOE_ERR_INVALID_ARG;
+  const WsPlan p = plan(L, T);
+  if (ws == nullptr || ws_bytes < p.total || !aligned(ws, kAlign)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* lg = logits;
+  if (x != nullptr) {
+    // the router's logits (its own top-k goes to scratch and is not used)
+    float* lo = logits ? logits : at<float>(ws, p.tlog);
+    if ((st = run_route(L, x, lo, T, at<int>(ws, p.ids), at<float>(ws, p.w), ws, p, s)) != MOE_OK)
+      return st;
+    lg = lo;
+  }
+  return hip_status(launch_table_route(token_ids, table, V, T, L->top_k, L->E, lg,
+                                       L->renormalize, topk_ids, topk_w, s));
 }
 
 int32_t moe_quantize_act(int32_t mode, const uint16_t* in, int32_t rows, int32_t K,

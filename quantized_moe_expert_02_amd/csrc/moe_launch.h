@@ -157,6 +157,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // and the decode top-k, for batches up to kRouterSlicedRows tokens: reads x,
 // wr, bias; writes part/apart (workspace), logits_out (optional), ids, w.
 hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s);
+// The fused decode's expert launches alone (gate/up + SwiGLU, down + combine)
+// on the routing in a.ids / a.w.
+hipError_t launch_decode_experts(const DecodeArgs& a, hipStream_t s);
+// Token-table routing on given logits [T][E] (k <= 64).
+hipError_t launch_table_route(const int* tok, const int* table, int V, int T, int k, int E,
+                              const float* logits, int renorm, int* ids, float* w, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------------
 hipError_t launch_combine(const float* y, const float* w, const int* pair_to_perm, const float* ys,

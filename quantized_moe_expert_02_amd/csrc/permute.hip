@@ -142,6 +142,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids
       pair_to_perm[p] = pos;
       // the last lane of each group advances the counter
       if ((same >> lane) == 1ull) cnt[e] = pos + 1;
+    } else if (p < p1) {
+      pair_to_perm[p] = -1;  // a dropped pair (expert id out of range)
     }
     __syncthreads();
   }

@@ -239,7 +239,57 @@ __global__ __launch_bounds__(kWave * kWaveTopkTokens) void topk_wave_kernel(Topk
   wave_topk(tk);
 }
 
+// Token-table routing: one wavefront per token; lane j < k takes table entry
+// j of the token's row; weights are the softmax (float64) of the logits at
+// the selected experts (renormalised over them, or the full softmax
+// gathered).  A token id outside [0, V) gives ids -1 and weights 0; an entry
+// outside [0, E) gets weight 0 and no part in the normalisation.
+constexpr int kTableTokens = 4;
+
+__global__ __launch_bounds__(kWave * kTableTokens) void table_route_kernel(
+    const int* __restrict__ tok, const int* __restrict__ table, int V, int T, int k, int E,
+    const float* __restrict__ logits, int renorm, int* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kTableTokens + (int)(threadIdx.x / kWave);
+  if (t >= T) return;  // a whole wavefront leaves together
+  const int v = tok[t];
+  const bool tok_ok = (unsigned)v < (unsigned)V;
+  int e = -1;
+  if (lane < k && tok_ok) e = table[(size_t)v * k + lane];
+  const bool ok = (unsigned)e < (unsigned)E;
+  const float* lrow = logits + (size_t)t * E;
+  const double l = ok ? static_cast<double>(lrow[e]) : 0.0;
+  double m;
+  double denom = 0.0;
+  if (renorm) {
+    m = ok ? l : -INFINITY;
+    for (int s = 32; s >= 1; s >>= 1) m = fmax(m, __shfl_xor(m, s, kWave));
+    double z = ok ? exp(l - m) : 0.0;
+    denom = z;
+    for (int s = 32; s >= 1; s >>= 1) denom += __shfl_xor(denom, s, kWave);
+  } else {
+    m = -INFINITY;
+    for (int i = lane; i < E; i += kWave) m = fmax(m, static_cast<double>(lrow[i]));
+    for (int s = 32; s >= 1; s >>= 1) m = fmax(m, __shfl_xor(m, s, kWave));
+    for (int i = lane; i < E; i += kWave) denom += exp(static_cast<double>(lrow[i]) - m);
+    for (int s = 32; s >= 1; s >>= 1) denom += __shfl_xor(denom, s, kWave);
+  }
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = tok_ok ? e : -1;
+    const double wj = (ok && denom > 0.0) ? exp(l - m) / denom : 0.0;
+    w[(size_t)t * k + lane] = static_cast<float>(wj);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_table_route(const int* tok, const int* table, int V, int T, int k, int E,
+                              const float* logits, int renorm, int* ids, float* w,
+                              hipStream_t s) {
+  if (k > kWave) return hipErrorInvalidValue;
+  return launch(table_route_kernel, dim3((T + kTableTokens - 1) / kTableTokens),
+                dim3(kWave * kTableTokens), 0, s, tok, table, V, T, k, E, logits, renorm, ids, w);
+}
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E,
                                 const RouterPlan& rp, float* part, float* amax, hipStream_t s) {

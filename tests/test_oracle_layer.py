@@ -259,3 +259,34 @@ def test_tiny_layer_end_to_end_vs_fsum_brute_force():
         assert np.allclose(res.out64[t], acc, rtol=1e-11, atol=1e-14)
         assert np.max(np.abs(res.out[t] - O.round_bf16(np.array(acc)))) <= \
             np.max(np.abs(acc)) * 2.0 ** -7
+
+
+def test_route_from_table_hand_worked():
+    """Token-table routing: experts from the table row of the token id, the
+    weights the softmax of the selected logits (closed form)."""
+    logits = np.array([[0.0, 1.0, 2.0, 3.0], [5.0, 4.0, 3.0, 2.0], [0.0, 0.0, 0.0, 0.0]])
+    table = np.array([[3, 0], [1, 2], [2, 9]])  # row 2 holds an entry outside [0, E)
+    ids, w = O.route_from_table([1, 0, 2], table, logits)
+    assert ids.tolist() == [[1, 2], [3, 0], [2, 9]]
+    e = np.exp(1.0)
+    assert np.allclose(w[0], [1 / (1 + e), e / (1 + e)], rtol=1e-15)
+    assert np.allclose(w[1], [1 / (1 + e ** 3), e ** 3 / (1 + e ** 3)], rtol=1e-15)  # logits 2, 5
+    assert w[2].tolist() == [1.0, 0.0]
+    ids, w = O.route_from_table([7, -1, 0], table, logits)   # token ids outside [0, V)
+    assert ids[0].tolist() == [-1, -1] and ids[1].tolist() == [-1, -1] and np.all(w[:2] == 0)
+    # full softmax gathered: weights sum to the selected share of the softmax
+    ids, w = O.route_from_table([0], table, logits[:1], renormalize=False)
+    z = np.exp(logits[0] - 3.0)
+    assert np.allclose(w[0], z[[3, 0]] / z.sum(), rtol=1e-15)
+
+
+def test_permute_drops_out_of_range_ids():
+    """Pairs whose expert id is outside [0, E) are dropped: counted nowhere,
+    placed after the sorted pairs, pair_to_perm -1; the rest is the stable
+    sort of the valid pairs."""
+    ids = np.array([[2, -1], [0, 5], [2, 0]], dtype=np.int32)   # E = 3
+    G = O.permute(ids, 3)
+    assert G.counts.tolist() == [2, 0, 2] and G.offsets.tolist() == [0, 2, 2, 4]
+    assert G.perm_to_pair[:4].tolist() == [2, 5, 0, 4]
+    assert G.pair_to_perm.tolist() == [2, -1, 0, -1, 3, 1]
+    assert sorted(G.perm_to_pair[4:].tolist()) == [1, 3]
