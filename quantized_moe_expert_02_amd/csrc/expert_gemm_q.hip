@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 // ---------------------------------------------------------------------------
 // The same GEMM with every operand moved global -> LDS by the LDS-DMA loads
 // (global_load_lds_dwordx4 / _dword): no staging registers, NST stages of LDS
-// in flight.  Taken when K % 128 == 0 (every step whole) and, for the MX
+// (one being computed, the next in flight).  Taken when K % 128 == 0 (every step whole) and, for the MX
 // modes, the weight scale words are aligned.
 //
 // A DMA instruction writes 64 lanes x 16 bytes to one contiguous KiB of LDS,
@@ -416,7 +416,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 template <int AM>
 struct DCfg {
   using C = QCfg<AM>;
-  static constexpr int NST = (AM == kActT128) ? 2 : 3;
+  // Stages of LDS in flight.  Measured at T=8192: two stages (50 KB for W4A8,
+  // 66 KB for 1x128) beat three or four, whose LDS leaves fewer workgroups
+  // per CU: more resident workgroups hide the step latency better than a
+  // deeper prefetch within one.
+  static constexpr int NST = 2;
   static constexpr int a_chunks = BM * C::a_bytes / 1024;  // KiB pieces per stage
   static constexpr int b_chunks = BN * C::b_bytes / 1024;
   static constexpr int a_per_wave = a_chunks / 4;
@@ -448,6 +452,21 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt_lds() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Wait until at most `later` stages of LOADS loads each are outstanding
+// (later in 0 .. MAXL; the wait count must be an immediate).
+template <int LOADS, int MAXL>
+__device__ __forceinline__ void wait_for_stage(int later) {
+  if constexpr (MAXL > 0) {
+    if (later >= MAXL) {
+      wait_vmcnt_lds<LOADS * MAXL>();
+      return;
+    }
+    wait_for_stage<LOADS, MAXL - 1>(later);
+  } else {
+    wait_vmcnt_lds<0>();
+  }
 }
 
 template <int AM, int OP>
@@ -619,12 +638,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       if (s0 < nk) issue(s0);
     for (int ks = 0; ks < nk; ++ks) {
       const int later = min(NST - 2, nk - 1 - ks);  // stages issued after ks
-      if constexpr (NST == 3) {
-        if (later >= 1) wait_vmcnt_lds<D::loads_per_stage>();
-        else wait_vmcnt_lds<0>();
-      } else {
-        wait_vmcnt_lds<0>();
-      }
+      wait_for_stage<D::loads_per_stage, NST - 2>(later);
       __builtin_amdgcn_s_barrier();
       if (ks + NST - 1 < nk) issue(ks + NST - 1);
       compute(ks, full_t);
