@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["moe_api.hip", "route.hip", "router_gemm.hip", "permute.hip", "expert_gemv.hip",
-           "expert_gemm.hip", "expert_gemm_q.hip", "quantize.hip", "decode.hip", "combine.hip"]
+           "expert_gemm.hip", "expert_gemm_d.hip", "expert_gemm_q.hip", "quantize.hip", "decode.hip", "combine.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.

@@ -111,6 +111,14 @@ constexpr int kGemmTileM = 128;
 hipError_t launch_grouped_gemm(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
                                const int* tiles, const int* n_tiles, int max_tiles,
                                const uint16_t* in, void* out, hipStream_t s);
+// The same GEMM for FP4 experts (MXFP4; NVFP4 down projections) with
+// K % 64 == 0 and aligned codes, scale words and activations (`in` 16-byte
+// aligned): operands moved by LDS-DMA and weight fragments decoded per
+// wavefront (launch_grouped_gemm takes it when it fits).
+bool grouped_gemm_dma_fits(int op, const WDesc& w0, const WDesc& w1);
+hipError_t launch_grouped_gemm_dma(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
+                                   const int* tiles, const int* n_tiles, int max_tiles,
+                                   const uint16_t* in, void* out, hipStream_t s);
 
 // ---- opt-in lossy activation modes -----------------------------------------
 // Quantize bf16 rows [rows][K] (K % 32 == 0) for mode kActMxfp8 / kActMxfp4 /
