@@ -237,13 +237,13 @@ def main():
         f"{k_tflops:.1f} TFLOP/s")
     if T <= GEMV_MAX_ROWS:
         # weights streamed once per group: bound by HBM
-        roof = {"kernel": "expert_gemv_kernel (routed gate/up + SwiGLU)",
+        roof = {"kernel": dominant_kernel_name(w, mode) + " (routed gate/up + SwiGLU)",
                 "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                 "avg_launch_us": round(k_avg_us, 3), "algorithmic_bytes_per_launch": k_bytes}
     elif not lossy:
         # bf16 x bf16 -> fp32 contraction on the matrix cores
-        roof = {"kernel": "grouped_gemm_kernel (routed gate/up + SwiGLU)",
+        roof = {"kernel": dominant_kernel_name(w, mode) + " (routed gate/up + SwiGLU)",
                 "bound": "mfma", "achieved": round(k_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "avg_launch_us": round(k_avg_us, 3), "algorithmic_flops_per_launch": k_flops,
@@ -357,7 +357,12 @@ def dominant_kernel_name(w, mode="exact"):
         base = "grouped_gemm_qd_kernel" if w.H % 128 == 0 else "grouped_gemm_q_kernel"
         return f"{base}<{ACT_MODES[mode][0]}, 0>"
     fmt = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3, "mxfp8": 4}[w.fmt]
-    base = "expert_gemv_kernel" if w.T <= GEMV_MAX_ROWS else "grouped_gemm_kernel"
+    if w.T <= GEMV_MAX_ROWS:
+        base = "expert_gemv_kernel"
+    elif w.fmt == "mxfp4" and w.H % 64 == 0:
+        base = "grouped_gemm_d_kernel"  # MXFP4 gate/up with whole 64-K steps: the LDS-DMA variant
+    else:
+        base = "grouped_gemm_kernel"
     return f"{base}<{fmt}, 0>"
 
 
@@ -367,7 +372,7 @@ def dominant_sources(T, mode="exact"):
     if T <= GEMV_MAX_ROWS:
         files += ["expert_gemv.hip"]
     else:
-        files += ["expert_gemm.hip"] if mode == "exact" else ["expert_gemm_q.hip"]
+        files += ["expert_gemm.hip", "expert_gemm_d.hip"] if mode == "exact" else ["expert_gemm_q.hip"]
     return [os.path.join(pkg, f) for f in files]
 
 
