@@ -18,31 +18,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= H) return;
-  // Issue the loads of 8 slots before summing them (one memory round trip
-  // per batch, not per slot); the sum stays in slot order.
-  constexpr int B = 8;
+  // All slots of a batch of 16 (every slot for k <= 16) in two round trips:
+  // the slots' rows and weights, then their y; the sum stays in slot order.
+  constexpr int B = 16;
+  // the shared expert's row, loaded with the first batch (added last)
+  const f32x4 yv = (ys != nullptr) ? *reinterpret_cast<const f32x4*>(ys + (size_t)t * H + n)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < k; j0 += B) {
-    f32x4 v[B];
+    int pp[B];
     float wj[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int j = min(j0 + b, k - 1);  // in bounds; slots past k are not summed
-      const int pp = p2p[(size_t)t * k + j];
-      wj[b] = w[(size_t)t * k + j];
-      // a dropped pair (pair_to_perm -1) contributes nothing
-      v[b] = (pp >= 0) ? *reinterpret_cast<const f32x4*>(y + (size_t)pp * H + n)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (pp < 0) wj[b] = 0.f;
+      pp[b] = -1;
+      wj[b] = 0.f;
+      if (j0 + b < k) {  // wave-uniform
+        pp[b] = p2p[(size_t)t * k + j0 + b];
+        wj[b] = w[(size_t)t * k + j0 + b];
+      }
     }
+    f32x4 v[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b)  // a dropped pair (pair_to_perm -1) contributes nothing
+      v[b] = (pp[b] >= 0) ? *reinterpret_cast<const f32x4*>(y + (size_t)pp[b] * H + n)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      if (j0 + b >= k) break;
+      if (j0 + b < k) {
+        const float wb = (pp[b] >= 0) ? wj[b] : 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj[b], v[b][q], acc[q]);
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(wb, v[b][q], acc[q]);
+      }
     }
   }
-  if (ys != nullptr) acc = acc + *reinterpret_cast<const f32x4*>(ys + (size_t)t * H + n);
+  if (ys != nullptr) acc = acc + yv;
   const uint2 o = make_uint2(f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16),
                              f32_to_bf16(acc[2]) | (uint32_t(f32_to_bf16(acc[3])) << 16));
   *reinterpret_cast<uint2*>(out + (size_t)t * H + n) = o;
