@@ -127,6 +127,28 @@ MIXED = {
 }
 
 
+# Every FP4 projection with K a multiple of 64, routed and shared, so that the
+# LDS-DMA grouped GEMM runs all of them (MXFP4 both projections, NVFP4 down)
+# at T > 64, the shared expert over its untiled rows included; Zipf groups
+# leave single-row and empty experts beside multi-tile ones.
+DMA = {
+    "mxfp4_all": synth.scaled(W["tiny_nvfp4_t4"], name="dma_mxfp4_all", T=150, H=512, E=10,
+                              I=192, top_k=3, fmt=synth.FMT_MXFP4, I_shared=128,
+                              shared_fmt=synth.FMT_MXFP4, zipf_s=1.1),
+    "nvfp4_all": synth.scaled(W["tiny_nvfp4_t4"], name="dma_nvfp4_all", T=150, H=384, E=10,
+                              I=320, top_k=2, fmt=synth.FMT_NVFP4, I_shared=192,
+                              shared_fmt=synth.FMT_NVFP4, zipf_s=1.1),
+}
+
+
+@pytest.mark.parametrize("name", list(DMA))
+def test_layer_dma_gemm(name):
+    w = DMA[name]
+    say(f"[gpu] LDS-DMA GEMM layer {name}: T={w.T} H={w.H} I={w.I} shared I={w.I_shared} "
+        f"fmt={w.fmt}/{w.shared_fmt}")
+    check_layer_against_oracle(layer_for(w), synth.make_x(w), what=name)
+
+
 # MXFP8 experts (E4M3 codes, E8M0 per 32): routed with ragged and with
 # 128-aligned K, and as the shared expert beside NVFP4 routed experts.
 MXFP8 = {
