@@ -248,29 +248,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
 
   const float ts0 = (FMT == FMT_NVFP4) ? p.w0.tscale[e] : 1.0f;
   const float ts1 = (FMT == FMT_NVFP4) ? p.w1.tscale[e] : 1.0f;
+  // ---- epilogue: the tile goes through LDS so that the stores are 16-byte
+  // vectors covering whole row segments (a fragment lane holds one column of
+  // four rows; storing from the fragments writes 4-byte pieces).  The K
+  // loop's LDS is free once every wavefront has passed the barrier.
   const int col = lane & 15;
+  __syncthreads();
+  if constexpr (OP == kOpGateUp) {
+    // h tile: 128 rows x 64 bf16 columns, one pass; staged rows of 72 bf16
+    constexpr int P = 72;
+    uint16_t* st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = m0 + 64 * wm + 16 * r + 4 * (lane >> 4) + j;
-      if (row >= m1) continue;
-      if constexpr (OP == kOpGateUp) {
+      for (int j = 0; j < 4; ++j) {
+        const int lr = 64 * wm + 16 * r + 4 * (lane >> 4) + j;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const int n = nt * (BN / 2) + 32 * wn + 16 * c + col;
-          if (n >= N) continue;
           const float hv = silu_fast(acc[r][c][j] * ts0) * (acc[r][c + 2][j] * ts1);
-          reinterpret_cast<uint16_t*>(p.out)[(size_t)row * N + n] = f32_to_bf16(hv);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int n = n0 + 64 * wn + 16 * c + col;
-          if (n >= N) continue;
-          reinterpret_cast<float*>(p.out)[(size_t)row * N + n] = acc[r][c][j] * ts0;
+          st[lr * P + 32 * wn + 16 * c + col] = f32_to_bf16(hv);
         }
       }
+    __syncthreads();
+    // thread -> (row tid / 8 + 32 q, 8 columns at 8 * (tid % 8))
+    const int cb = 8 * (tid & 7);
+    const int n = nt * (BN / 2) + cb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = (tid >> 3) + 32 * q;
+      const int row = m0 + lr;
+      if (row >= m1) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + lr * P + cb);
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (size_t)row * N + n;
+      if (n + 7 < N) {
+        *reinterpret_cast<u32x4*>(o) = v;
+      } else {
+        const uint16_t* hs = reinterpret_cast<const uint16_t*>(&v);
+        for (int i = 0; i < 8; ++i)
+          if (n + i < N) o[i] = hs[i];
+      }
+    }
+  } else {
+    // y tile: 128 rows x 128 fp32 columns in two halves of 64 rows; staged
+    // rows of 132 floats (the fragment writes of the four 16-lane groups
+    // land in distinct banks)
+    constexpr int P = 132;
+    float* st = reinterpret_cast<float*>(lds);
+    const int cb = 4 * (tid & 31);
+    const int n = n0 + cb;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              st[(16 * r + 4 * (lane >> 4) + j) * P + 64 * wn + 16 * c + col] = acc[r][c][j] * ts0;
+      }
+      __syncthreads();
+      // thread -> (row tid / 32 + 8 q, 4 columns at 4 * (tid % 32)); N % 4 == 0
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int lr = (tid >> 5) + 8 * q;
+        const int row = m0 + 64 * half + lr;
+        if (row < m1 && n < N)
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (size_t)row * N + n) =
+              *reinterpret_cast<const f32x4*>(st + lr * P + cb);
+      }
+      if (half == 0) __syncthreads();
     }
   }
 }
@@ -295,6 +342,8 @@ bool grouped_gemm_dma_fits(int op, const WDesc& w0, const WDesc& w1) {
   // loop of gate/up; on the short K of the down projection this kernel wins.
   const bool fmt_ok = w0.fmt == FMT_MXFP4 || (w0.fmt == FMT_NVFP4 && op == kOpDown);
   if (!fmt_ok || w1.fmt != w0.fmt || w0.cols % BK != 0) return false;
+  // the epilogue stores aligned 16-byte column groups: 8 bf16 of h, 4 fp32 of y
+  if (w0.rows % ((op == kOpGateUp) ? 8 : 4) != 0) return false;
   // the scale word of a step (4 bytes NVFP4, 2 bytes MXFP4) is one aligned DMA
   // and the 16-byte code pieces are aligned DMAs too
   const uintptr_t a = (w0.fmt == FMT_NVFP4) ? 4 : 2;
