@@ -650,13 +650,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     main_loop(std::false_type{});
 
   const int col = lane & 15;
+  if constexpr (OP == kOpGateUp) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 4; ++r) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = m0 + 64 * wm + 16 * r + 4 * (lane >> 4) + j;
-      if (row >= m1) continue;
-      if constexpr (OP == kOpGateUp) {
+      for (int j = 0; j < 4; ++j) {
+        const int row = m0 + 64 * wm + 16 * r + 4 * (lane >> 4) + j;
+        if (row >= m1) continue;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int n = nt * (BN / 2) + 32 * wn + 16 * c + col;
@@ -664,14 +664,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
           const float hv = silu_fast(acc[r][c][j]) * acc[r][c + 2][j];
           reinterpret_cast<uint16_t*>(p.out)[(size_t)row * N + n] = f32_to_bf16(hv);
         }
-      } else {
+      }
+    }
+  } else {
+    // fp32 y through the K loop's LDS, two halves of 64 rows x 132-float
+    // rows, stored as 16-byte vectors over whole row segments (a fragment
+    // lane holds one column of four rows: storing from the fragments writes
+    // 4-byte pieces); N not a multiple of 4 falls back to elements.
+    constexpr int P = 132;
+    static_assert(64 * P * 4 <= NST * D::stage_bytes, "staged half tile fits");
+    float* st = reinterpret_cast<float*>(lds);
+    const int cb = 4 * (tid & 31);
+    const int n = n0 + cb;
+    const bool vec = N % 4 == 0;
+    __syncthreads();
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int n = n0 + 64 * wn + 16 * c + col;
-          if (n >= N) continue;
-          reinterpret_cast<float*>(p.out)[(size_t)row * N + n] = acc[r][c][j];
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              st[(16 * r + 4 * (lane >> 4) + j) * P + 64 * wn + 16 * c + col] = acc[r][c][j];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int lr = (tid >> 5) + 8 * q;
+        const int row = m0 + 64 * half + lr;
+        if (row >= m1 || n >= N) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(st + lr * P + cb);
+        float* o = reinterpret_cast<float*>(p.out) + (size_t)row * N + n;
+        if (vec && n + 3 < N) {
+          *reinterpret_cast<f32x4*>(o) = v;
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (n + i < N) o[i] = v[i];
         }
       }
+      if (half == 0) __syncthreads();
     }
   }
 }
