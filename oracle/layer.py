@@ -1,9 +1,9 @@
 """The routed mixture-of-experts layer in float64 — TEST INFRASTRUCTURE.
 
-Steps, in the order the layer runs them (the pages name the layer and its
-kernels — "DGPP" README, source layout: "GEMV and GEMM for each weight
-format ... MoE" — but print none of its arithmetic; where they are silent the
-reading taken is stated here and in the design doc):
+Steps, in the order the layer runs them (the pages name the layer and list
+per-format GEMV and GEMM kernels for it — "DGPP" README, source layout — but
+print none of its arithmetic; where they are silent the reading taken is
+stated here):
 
 1. router logits  l[t,e] = sum_h x[t,h] * Wr[h,e] + b[e]   (x bf16, Wr fp32
    [H][E], b an optional per-expert logit offset).  Routing is decided on the
