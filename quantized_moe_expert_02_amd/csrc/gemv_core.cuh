@@ -1,9 +1,9 @@
 // Expert GEMV core for small row groups (decode): weights streamed once per
 // group, decoded in registers, contracted on the bf16 matrix cores.
 //
-// "Decode on the Spark is a memory-bandwidth problem" and the decode kernels
-// read the weights at the memory's line rate (forum thread "DGPP: a
-// GB10-optimized C++/CUDA inference engine", the "Lossless bf12" post); the
+// Decode is bound by memory bandwidth, and the decode kernels read the
+// weights at the memory's line rate (forum thread "DGPP: a GB10-optimized
+// C++/CUDA inference engine", the "Lossless bf12" post); the
 // expert kernels are written per weight format and read the checkpoint bytes
 // with no dequantized copy ("DGPP" README, intro bullet on checkpoint formats).
 //

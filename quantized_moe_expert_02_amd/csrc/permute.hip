@@ -1,12 +1,12 @@
 // Token-to-expert grouping: a stable counting sort of the (token, slot) pairs.
 //
-// The grouped expert GEMM runs "over a compact list of the routed segments'
-// tiles instead of a grid over the longest segment" (gitee "dgpp" README,
-// "Execution and performance", engine.expert_tile_list).  The segments are
-// built here deterministically: counts come from per-chunk histograms (LDS
-// integer atomics, order-free), offsets from a scan, and each pair's rank in
-// its segment from a scan over chunks plus an in-order rank within the chunk,
-// so the permutation is the same on every run.
+// The grouped expert GEMM walks a compact list of the tiles the routed
+// segments actually hold, not a grid sized by the longest segment (gitee
+// "dgpp" README, "Execution and performance", engine.expert_tile_list).  The
+// segments are built here deterministically: counts come from per-chunk
+// histograms (LDS integer atomics, order-free), offsets from a scan, and each
+// pair's rank in its segment from a scan over chunks plus an in-order rank
+// within the chunk, so the permutation is the same on every run.
 #include "moe_launch.h"
 
 namespace moe {
