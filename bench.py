@@ -359,8 +359,8 @@ def dominant_kernel_name(w, mode="exact"):
     fmt = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3, "mxfp8": 4}[w.fmt]
     if w.T <= GEMV_MAX_ROWS:
         base = "expert_gemv_kernel"
-    elif w.fmt == "mxfp4" and w.H % 64 == 0:
-        base = "grouped_gemm_d_kernel"  # MXFP4 gate/up with whole 64-K steps: the LDS-DMA variant
+    elif w.fmt in ("nvfp4", "mxfp4") and w.H % 64 == 0:
+        base = "grouped_gemm_d_kernel"  # FP4 gate/up with whole 64-K steps: the LDS-DMA variant
     else:
         base = "grouped_gemm_kernel"
     return f"{base}<{fmt}, 0>"

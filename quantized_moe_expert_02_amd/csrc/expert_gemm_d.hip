@@ -115,6 +115,12 @@ __device__ __forceinline__ bf16x8 decode_frag(uint32_t d, uint32_t sbyte) {
   return r.v;
 }
 
+template <int FMT>
+struct DWaves {
+  static constexpr int KWM = (FMT == FMT_NVFP4) ? 1 : 2, KWN = 4 / KWM;
+  static constexpr int R = BM / KWM / 16, C = BN / KWN / 16;
+};
+
 template <int FMT, int OP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void grouped_gemm_d_kernel(
     DParams p) {
@@ -184,19 +190,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     dma<D::s_row>(ssrc + ks * D::s_row, st + sdst);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
-  int bcol[4];
+  // Wavefront grid KWM x KWN over the 128 x 128 tile; each wavefront holds R x
+  // C fragments of 16 x 16.  MXFP4: 2 x 2 (64 x 64 each).  NVFP4: 1 x 4 (128
+  // rows x 32 weight rows each), so that every B fragment, whose decode
+  // multiplies by the E4M3 scale in fp32, is decoded by one wavefront only,
+  // at the price of reading each A fragment four times from LDS instead of
+  // twice.  Gate/up: a wavefront's columns are C/2 gate fragments and the
+  // C/2 matching up fragments.
+  using L = DWaves<FMT>;
+  constexpr int R = L::R, C = L::C;
+  const int wm = wave / L::KWN, wn = wave % L::KWN;
+  constexpr int kWaveRows = BM / L::KWM, kWaveCols = BN / L::KWN;
+  int bcol[C];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    bcol[c] = (OP == kOpGateUp) ? ((c < 2) ? 32 * wn + 16 * c : 64 + 32 * wn + 16 * (c - 2))
-                                : 64 * wn + 16 * c;
-  f32x4 acc[4][4];
+  for (int c = 0; c < C; ++c)
+    bcol[c] = (OP == kOpGateUp)
+                  ? ((c < C / 2) ? (kWaveCols / 2) * wn + 16 * c
+                                 : BN / 2 + (kWaveCols / 2) * wn + 16 * (c - C / 2))
+                  : kWaveCols * wn + 16 * c;
+  f32x4 acc[R][C];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int vrows = m1 - m0 - 64 * wm;
-  const int vr = vrows <= 0 ? 0 : min(4, (vrows + 15) / 16);
+    for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int vrows = m1 - m0 - kWaveRows * wm;
+  const int vr = vrows <= 0 ? 0 : min(R, (vrows + 15) / 16);
   const int g = lane >> 4, lr = lane & 15;
 
   auto compute = [&](int ks, auto full_t) {
@@ -206,9 +224,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     for (int kk = 0; kk < BK; kk += 32) {
       // B fragments: row bcol[c] + lr, K kk + 8g .. +8: 4 code bytes at byte
       // 4g of the row's 16-byte piece kk / 32, and the scale byte of that K
-      bf16x8 bfr[4];
+      bf16x8 bfr[C];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < C; ++c) {
         const int row = bcol[c] + lr;
         const int slot = (kk >> 5) ^ ((row >> 3) & 1);
         const uint32_t d = *reinterpret_cast<const uint32_t*>(st + D::b_off + row * 32 + 16 * slot + 4 * g);
@@ -217,13 +235,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
         bfr[c] = decode_frag<FMT>(d, sbyte);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < R; ++r) {
         if (!FULL && r >= vr) continue;
-        const int row = 64 * wm + 16 * r + lr;
+        const int row = kWaveRows * wm + 16 * r + lr;
         const int slot = ((kk >> 3) + g) ^ ((row >> 1) & 7);
         const bf16x8 af = *reinterpret_cast<const bf16x8*>(st + D::a_off + row * 128 + 16 * slot);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < C; ++c)
           acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[c], acc[r][c], 0, 0, 0);
       }
     }
@@ -259,14 +277,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     constexpr int P = 72;
     uint16_t* st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int lr = 64 * wm + 16 * r + 4 * (lane >> 4) + j;
+        const int lr = kWaveRows * wm + 16 * r + 4 * (lane >> 4) + j;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float hv = silu_fast(acc[r][c][j] * ts0) * (acc[r][c + 2][j] * ts1);
-          st[lr * P + 32 * wn + 16 * c + col] = f32_to_bf16(hv);
+        for (int c = 0; c < C / 2; ++c) {
+          const float hv = silu_fast(acc[r][c][j] * ts0) * (acc[r][c + C / 2][j] * ts1);
+          st[lr * P + (kWaveCols / 2) * wn + 16 * c + col] = f32_to_bf16(hv);
         }
       }
     __syncthreads();
@@ -298,14 +316,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     const int n = n0 + cb;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      if (wm == half) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < R; ++r) {
+        const int r0 = kWaveRows * wm + 16 * r;  // first tile row of fragment row r
+        if ((r0 >> 6) != half) continue;
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < C; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              st[(16 * r + 4 * (lane >> 4) + j) * P + 64 * wn + 16 * c + col] = acc[r][c][j] * ts0;
+          for (int j = 0; j < 4; ++j)
+            st[(r0 - 64 * half + 4 * (lane >> 4) + j) * P + kWaveCols * wn + 16 * c + col] =
+                acc[r][c][j] * ts0;
       }
       __syncthreads();
       // thread -> (row tid / 32 + 8 q, 4 columns at 4 * (tid % 32)); N % 4 == 0
@@ -335,12 +355,8 @@ hipError_t launch_d(DParams p, int n_row_tiles, hipStream_t s) {
 }  // namespace
 
 bool grouped_gemm_dma_fits(int op, const WDesc& w0, const WDesc& w1) {
-  // Measured choice: an MXFP4 fragment decodes in 4 conversions, an NVFP4 one
-  // needs the E4M3 scale multiplied in fp32 (the scaled converters keep only
-  // the exponent of their scale), and decoding every fragment twice then
-  // costs more than the register-staged kernel's single decode on the long K
-  // loop of gate/up; on the short K of the down projection this kernel wins.
-  const bool fmt_ok = w0.fmt == FMT_MXFP4 || (w0.fmt == FMT_NVFP4 && op == kOpDown);
+  // FP4 only: the 16-byte code pieces of a step are 64 K of one row.
+  const bool fmt_ok = w0.fmt == FMT_MXFP4 || w0.fmt == FMT_NVFP4;
   if (!fmt_ok || w1.fmt != w0.fmt || w0.cols % BK != 0) return false;
   // the epilogue stores aligned 16-byte column groups: 8 bf16 of h, 4 fp32 of y
   if (w0.rows % ((op == kOpGateUp) ? 8 : 4) != 0) return false;

@@ -111,7 +111,7 @@ constexpr int kGemmTileM = 128;
 hipError_t launch_grouped_gemm(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
                                const int* tiles, const int* n_tiles, int max_tiles,
                                const uint16_t* in, void* out, hipStream_t s);
-// The same GEMM for FP4 experts (MXFP4; NVFP4 down projections) with
+// The same GEMM for FP4 experts (NVFP4, MXFP4) with
 // K % 64 == 0, output rows a multiple of 8 (gate/up) or 4 (down) and aligned
 // codes, scale words and activations (`in` 16-byte aligned): operands moved by
 // LDS-DMA, weight fragments decoded per wavefront, the output tile stored
