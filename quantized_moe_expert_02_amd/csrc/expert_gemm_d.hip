@@ -29,23 +29,23 @@
 namespace moe {
 namespace {
 
-constexpr int BM = kGemmTileM, BN = 128, BK = 64;
+constexpr int BM = kGemmTileM, BN = 256, BK = 64;
 constexpr int kXcds = 8;
 constexpr int kStages = 2;
 
 template <int FMT>
 struct DLayout {
   static constexpr int a_off = 0;                   // [128 rows][128 B] bf16
-  static constexpr int b_off = BM * 128;            // [128 rows][32 B] E2M1 codes
+  static constexpr int b_off = BM * 128;            // [BN rows][32 B] E2M1 codes
   // Scale words of a step: NVFP4 4 bytes, MXFP4 2 bytes per weight row.  A
   // DMA of 4 bytes or fewer lands at a 4-byte pitch per lane (M0 + 4 * lane),
   // so each row has a 4-byte slot whatever the word's size.
   static constexpr int s_off = b_off + BN * 32;
   static constexpr int s_row = (FMT == FMT_NVFP4) ? 4 : 2;  // bytes loaded per row
   static constexpr int s_pitch = 4;                          // LDS bytes per row
-  static constexpr int s_bytes = 2 * 64 * s_pitch;           // two 64-lane DMA regions
-  static constexpr int stage = s_off + s_bytes + 512;  // + one dummy region for waves 2-3
-  static constexpr int loads = 4 + 1 + 1;           // per wave and stage: A, B, scale
+  static constexpr int s_bytes = BN * s_pitch;               // one 64-lane region per wave
+  static constexpr int stage = s_off + s_bytes;
+  static_assert(BN == 4 * 64, "each wavefront DMAs the scale words of 64 weight rows");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -124,7 +124,7 @@ struct DWaves {
 };
 
 template <int FMT, int OP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void grouped_gemm_d_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_d_kernel(
     DParams p) {
   using D = DLayout<FMT>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * D::stage];
@@ -161,34 +161,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     const int piece = (lane & 7) ^ ((r >> 1) & 7);
     asrc[i] = p.in + (size_t)input_row<OP>(p, m0 + r, m0, m1) * K + 8 * piece;
   }
-  // B codes: KiB-chunks of 32 rows x 32 B; wave w takes chunk w.
-  const uint8_t* bsrc;
-  {
-    const int r = 32 * wave + (lane >> 1);
+  // B codes: KiB-chunks of 32 rows x 32 B; wave w takes chunks 2w, 2w+1.
+  const uint8_t* bsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 64 * wave + 32 * i + (lane >> 1);
     const int piece = (lane & 1) ^ ((r >> 3) & 1);
     const WDesc& wq = (OP == kOpGateUp && r >= BN / 2) ? p.w1 : p.w0;
     const int wr0 = (OP == kOpGateUp) ? n0 + (r & (BN / 2 - 1)) : n0 + r;
     const int wr = wr0 < N ? wr0 : N - 1;
-    bsrc = wq.codes + e * wq.stride_codes + (size_t)wr * (K / 2) + 16 * piece;
+    bsrc[i] = wq.codes + e * wq.stride_codes + (size_t)wr * (K / 2) + 16 * piece;
   }
-  // scale words: waves 0-1 the weight rows 64w + lane (waves 2-3 repeat
-  // wave 0's into a region nobody reads, so every wave issues the same loads)
+  // scale words: wave w the weight rows 64w + lane
   const uint8_t* ssrc;
   {
-    const int r = 64 * (wave & 1) + lane;
+    const int r = 64 * wave + lane;
     const WDesc& wq = (OP == kOpGateUp && r >= BN / 2) ? p.w1 : p.w0;
     const int wr0 = (OP == kOpGateUp) ? n0 + (r & (BN / 2 - 1)) : n0 + r;
     const int wr = wr0 < N ? wr0 : N - 1;
     ssrc = reinterpret_cast<const uint8_t*>(wq.scales) + e * wq.stride_scales +
            (size_t)wr * (K / (FMT == FMT_NVFP4 ? 16 : 32));
   }
-  const int sdst = (wave < 2) ? D::s_off + 64 * D::s_pitch * wave : D::s_off + D::s_bytes;
+  const int sdst = D::s_off + 64 * D::s_pitch * wave;
 
   auto issue = [&](int ks) {
     uint8_t* st = lds + (ks % kStages) * D::stage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma<16>(asrc[i] + ks * BK, st + D::a_off + 1024 * (4 * wave + i));
-    dma<16>(bsrc + ks * (BK / 2), st + D::b_off + 1024 * wave);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma<16>(bsrc[i] + ks * (BK / 2), st + D::b_off + 1024 * (2 * wave + i));
     dma<D::s_row>(ssrc + ks * D::s_row, st + sdst);
   };
 
@@ -275,8 +276,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
   const int col = lane & 15;
   __syncthreads();
   if constexpr (OP == kOpGateUp) {
-    // h tile: 128 rows x 64 bf16 columns, one pass; staged rows of 72 bf16
-    constexpr int P = 72;
+    // h tile: BM rows x BN/2 bf16 columns, one pass; staged rows of BN/2 + 8
+    constexpr int HW = BN / 2, P = HW + 8;
+    static_assert(BM * P * 2 <= kStages * D::stage, "staged h tile fits");
     uint16_t* st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -290,12 +292,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
         }
       }
     __syncthreads();
-    // thread -> (row tid / 8 + 32 q, 8 columns at 8 * (tid % 8))
-    const int cb = 8 * (tid & 7);
-    const int n = nt * (BN / 2) + cb;
+    // thread -> (row tid / TPR + RPP q, 8 columns at 8 * (tid % TPR))
+    constexpr int TPR = HW / 8, RPP = 256 / TPR;
+    const int cb = 8 * (tid % TPR);
+    const int n = nt * HW + cb;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lr = (tid >> 3) + 32 * q;
+    for (int q = 0; q < BM / RPP; ++q) {
+      const int lr = tid / TPR + RPP * q;
       const int row = m0 + lr;
       if (row >= m1) continue;
       const u32x4 v = *reinterpret_cast<const u32x4*>(st + lr * P + cb);
@@ -309,37 +312,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
       }
     }
   } else {
-    // y tile: 128 rows x 128 fp32 columns in two halves of 64 rows; staged
-    // rows of 132 floats (the fragment writes of the four 16-lane groups
-    // land in distinct banks)
-    constexpr int P = 132;
+    // y tile: BM rows x BN fp32 columns in parts of QR rows; staged rows of
+    // BN + 4 floats (the fragment writes of the four 16-lane groups land in
+    // distinct banks)
+    constexpr int P = BN + 4, QR = (BN == 256) ? 32 : 64;
+    static_assert(QR * P * 4 <= kStages * D::stage, "staged part of the y tile fits");
     float* st = reinterpret_cast<float*>(lds);
-    const int cb = 4 * (tid & 31);
+    constexpr int TPR = BN / 4, RPP = 256 / TPR;
+    const int cb = 4 * (tid % TPR);
     const int n = n0 + cb;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int part = 0; part < BM / QR; ++part) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int r0 = kWaveRows * wm + 16 * r;  // first tile row of fragment row r
-        if ((r0 >> 6) != half) continue;
+        if (r0 / QR != part) continue;
 #pragma unroll
         for (int c = 0; c < C; ++c)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            st[(r0 - 64 * half + 4 * (lane >> 4) + j) * P + kWaveCols * wn + 16 * c + col] =
+            st[(r0 - QR * part + 4 * (lane >> 4) + j) * P + kWaveCols * wn + 16 * c + col] =
                 acc[r][c][j] * ts0;
       }
       __syncthreads();
-      // thread -> (row tid / 32 + 8 q, 4 columns at 4 * (tid % 32)); N % 4 == 0
+      // thread -> (row tid / TPR + RPP q, 4 columns at 4 * (tid % TPR)); N % 4 == 0
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int lr = (tid >> 5) + 8 * q;
-        const int row = m0 + 64 * half + lr;
+      for (int q = 0; q < QR / RPP; ++q) {
+        const int lr = tid / TPR + RPP * q;
+        const int row = m0 + QR * part + lr;
         if (row < m1 && n < N)
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (size_t)row * N + n) =
               *reinterpret_cast<const f32x4*>(st + lr * P + cb);
       }
-      if (half == 0) __syncthreads();
+      if (part + 1 < BM / QR) __syncthreads();
     }
   }
 }
