@@ -3,20 +3,22 @@
 // each wavefront decodes its own weight fragments from the raw checkpoint
 // codes in LDS.
 //
-// Same tiles, rows, epilogues and exact chain as grouped_gemm_kernel (128
-// permuted rows x 128 weight rows, 4 wavefronts of 64x64 on
-// v_mfma_f32_16x16x32_bf16, K in steps of 64; weights decoded to bf16 exactly:
-// NVFP4 E2M1 x E4M3 block scale, MXFP4 E2M1 x E8M0), but:
+// The rows, exact chain and epilogue arithmetic of grouped_gemm_kernel
+// (weights decoded to bf16 exactly: NVFP4 E2M1 x E4M3 block scale, MXFP4
+// E2M1 x E8M0; v_mfma_f32_16x16x32_bf16, K in steps of 64), on tiles of 128
+// permuted rows x 256 weight rows (gate/up: 128 gate + the matching 128 up
+// rows), but:
 //
 // * no staging registers: bf16 activation rows (gathered through
 //   perm_to_pair), the packed E2M1 codes and the block-scale words of a step
 //   are DMA'd into LDS (global_load_lds), two stages, one bare barrier per
 //   step after an explicit vmcnt wait;
-// * the weight tile stays packed in LDS (4 KiB per step instead of 16 KiB of
-//   bf16); a wavefront reads the 4 bytes (8 codes) of each B fragment and the
-//   fragment's scale byte and decodes them in registers.  A fragment is
-//   decoded by both wavefronts that use it, in exchange for the registers
-//   and LDS that let three workgroups share a CU.
+// * the weight tile stays packed in LDS (8 KiB per step instead of 32 KiB of
+//   bf16); on a 1 x 4 wavefront grid (128 rows x 64 weight rows each) a
+//   wavefront reads the 4 bytes (8 codes) and the scale byte of each of its B
+//   fragments and decodes them in registers, so every fragment is decoded
+//   once;
+// * the output tile leaves through LDS as 16-byte row vectors.
 //
 // LDS rows are unpadded (a DMA instruction fills one contiguous KiB) and the
 // 16-byte pieces are XOR-swizzled per row: piece P of a 128-byte activation
