@@ -74,14 +74,6 @@ def test_layer_decode_full(name):
         f"unique experts={len(np.unique(r['ids']))}")
 
 
-def test_layer_decode_fp8_wide_sampled():
-    w = W["decode_t8_fp8_wide"]
-    say("[gpu] layer decode_t8_fp8_wide (full size, outputs of tokens 0 and 5)")
-    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), tokens=[0, 5],
-                                   what="decode_t8_fp8_wide")
-    say(f"[gpu] fp8 wide: rel={r['rel']:.2e} worst={r['worst']:.2e}")
-
-
 # The 9-64 row band (speculative-verify and batched-decode sizes): sliced
 # router, block top-k, expert GEMV in 16-row passes (groups above 16 rows
 # under the Zipf router), shared expert over up to 4 passes.
@@ -444,20 +436,6 @@ def test_expert_gemm_and_combine_units(name):
     assert_close(O.bf16_value(bf16_bits(out)), ref.out, name + " combine")
 
 
-def test_layer_prefill_full_sampled():
-    """Prefill chunk at full size: routing of all 8192 tokens bit-exact,
-    outputs of sampled tokens within tolerance."""
-    w = W["prefill_t8192_nvfp4_zipf"]
-    say("[gpu] layer prefill_t8192_nvfp4_zipf (full size, 8 sampled outputs)")
-    toks = [0, 1, 777, 2048, 4095, 5000, 8000, 8191]
-    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), tokens=toks,
-                                   what="prefill_t8192_nvfp4_zipf")
-    counts = np.bincount(r["ids"].reshape(-1), minlength=w.E)
-    say(f"[gpu] prefill: rel={r['rel']:.2e} worst={r['worst']:.2e} empty experts="
-        f"{int((counts == 0).sum())} max group={int(counts.max())} recomputed={r['recomputed']}")
-    assert (counts == 0).sum() > 0          # Zipf popularity leaves some experts idle
-
-
 def test_workspace_reuse_across_batch_sizes():
     """One zero-filled workspace, calls with T = 8, 1, 5, 8 in a row: the fused
     decode kernels leave their counters zero, so every call stays exact."""
@@ -486,7 +464,7 @@ def _degenerate_layer(fmt, H=352, I=160):
     scales, maximum-magnitude codes, an all-zero expert, a zero tensor scale,
     and a NaN block scale in the shared expert's down projection."""
     import dataclasses
-    w = synth.scaled(W["tiny_nvfp4_t4"], name=f"degenerate_{fmt}_{H}_{I}", T=80, H=H, E=8, I=I,
+    w = synth.scaled(W["tiny_nvfp4_t4"], name=f"degenerate_{fmt}_{H}_{I}", T=150, H=H, E=8, I=I,
                      top_k=5, fmt=fmt, I_shared=96, shared_fmt=synth.FMT_FP8)
     L = layer_for(w)
 
@@ -538,11 +516,13 @@ def test_degenerate_weights(fmt, T):
 
 
 @pytest.mark.parametrize("fmt", [synth.FMT_NVFP4, synth.FMT_MXFP4])
-@pytest.mark.parametrize("T", [5, 12])
+@pytest.mark.parametrize("T", [5, 12, 80, 150])
 def test_degenerate_weights_aligned(fmt, T):
     """The same degenerate values with K a multiple of 128, where the FP4
     block scales are read by whole chunk (fused decode at T = 5, the
-    small-group expert GEMM at T = 12)."""
+    small-group expert GEMV at T = 12) and every FP4 projection of the
+    grouped GEMM runs the LDS-DMA kernel (T = 80, 150: groups of one and two
+    128-row tiles)."""
     w, L = _degenerate_layer(fmt, H=512, I=256)
     x_bits = synth.make_x(w)[:T]
     say(f"[gpu] degenerate weights (aligned K) fmt={fmt} T={T}")

@@ -32,6 +32,24 @@ def _all_bf16_values():
     return vals, bits[fin][np.unique(v[fin], return_index=True)[1]]
 
 
+def test_bf16_value_matches_torch_on_every_pattern():
+    """bf16_value against torch's own bfloat16 -> float64 conversion, all
+    65,536 bit patterns (NaN patterns compared as NaN, signed zeros by sign)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.bf16_value(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # anchors: 1.0, -2.0, the largest finite, the smallest subnormal, +inf
+    assert O.bf16_value(np.uint16(0x3F80)) == 1.0
+    assert O.bf16_value(np.uint16(0xC000)) == -2.0
+    assert O.bf16_value(np.uint16(0x7F7F)) == (2.0 - 2.0 ** -7) * 2.0 ** 127
+    assert O.bf16_value(np.uint16(0x0001)) == 2.0 ** -133
+    assert O.bf16_value(np.uint16(0x7F80)) == math.inf
+
+
 def test_round_bf16_brute_force_nearest_ties_even():
     vals, bits = _all_bf16_values()           # every non-negative finite bf16
     rng = np.random.default_rng(0)
