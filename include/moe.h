@@ -294,6 +294,25 @@ int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int
                                  const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                                  void* ws, size_t ws_bytes, int32_t act_mode, void* stream);
 
+/* ---- the layer without a caller workspace ------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture that must not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation.  moe_layer_forward (MOE_ACT_EXACT, no debug outputs)
+ * with its workspace taken from one fixed array inside the library, of
+ * moe_noalloc_workspace_limit() bytes (32 MiB) per GPU, held by each GPU the
+ * call runs on until the process ends.  The call allocates and frees
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Returns MOE_ERR_WORKSPACE, before any launch, when the layer at this T
+ *   needs more workspace than the array holds (moe_workspace_size(L, T) >
+ *   moe_noalloc_workspace_limit(); at H = 2048, E = 512, I = 512, top-10
+ *   that is above roughly T = 350 tokens); other errors as moe_layer_forward.
+ *   Every call on a GPU shares that GPU's array, which keeps the last call's
+ *   contents (no kernel reads a workspace byte before writing it in the same
+ *   call): calls that overlap in time on one GPU, on any streams, race. */
+size_t moe_noalloc_workspace_limit(void);
+int32_t moe_layer_forward_noalloc(const moe_layer_desc* L, const uint16_t* x, int32_t T,
+                                  uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

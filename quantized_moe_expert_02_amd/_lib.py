@@ -36,7 +36,8 @@ MOE_ACT_FP8_T128 = 3
 EXPORTED = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_validate_layer", "moe_workspace_size",
             "moe_route_topk", "moe_permute_workspace_size", "moe_permute", "moe_expert_gemm",
             "moe_combine", "moe_layer_forward", "moe_quantize_act", "moe_expert_gemm_q",
-            "moe_layer_forward_ex", "moe_route_table", "moe_layer_forward_routed"]
+            "moe_layer_forward_ex", "moe_route_table", "moe_layer_forward_routed",
+            "moe_noalloc_workspace_limit", "moe_layer_forward_noalloc"]
 
 
 class MoeError(RuntimeError):
@@ -90,6 +91,8 @@ def _load():
         "moe_layer_forward_ex": (I32, [LP, P, I32, P, P, SZ, I32, P, P, P, P]),
         "moe_route_table": (I32, [LP, P, P, P, P, I32, I32, P, P, P, SZ, P]),
         "moe_layer_forward_routed": (I32, [LP, P, I32, P, P, P, P, SZ, I32, P]),
+        "moe_noalloc_workspace_limit": (SZ, []),
+        "moe_layer_forward_noalloc": (I32, [LP, P, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -218,3 +221,12 @@ def moe_layer_forward_routed(L, x, T, topk_ids, topk_w, out, ws, act_mode=0, ws_
     st = LIB.moe_layer_forward_routed(ctypes.byref(L), _p(x), T, _p(topk_ids), _p(topk_w), _p(out),
                                       _p(ws), wsb, act_mode, _stream(stream))
     return _check(st, "moe_layer_forward_routed") if check else st
+
+
+def moe_noalloc_workspace_limit() -> int:
+    return LIB.moe_noalloc_workspace_limit()
+
+
+def moe_layer_forward_noalloc(L, x, T, out, stream=None, check=True):
+    st = LIB.moe_layer_forward_noalloc(ctypes.byref(L), _p(x), T, _p(out), _stream(stream))
+    return _check(st, "moe_layer_forward_noalloc") if check else st

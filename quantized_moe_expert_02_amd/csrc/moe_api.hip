@@ -7,6 +7,7 @@
 // negative status comes back before any launch, and the caller sizes the
 // workspace from moe_workspace_size() up front.
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "moe_launch.h"
@@ -14,6 +15,17 @@
 using namespace moe;
 
 namespace {
+
+// Workspace of moe_layer_forward_noalloc: one array per GPU the library runs
+// on, held until the process ends.  Host code never uses the array's name
+// as an address (on the host it is a stand-in, not device memory): the
+// device address is resolved once per device with hipGetSymbolAddress and
+// kept in scratch_addr.
+constexpr size_t kNoAllocBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -624,6 +636,40 @@ int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T,
                           float* dbg_w, void* stream) {
   return layer_impl(L, x, T, out, ws, ws_bytes, MOE_ACT_EXACT, dbg_logits, dbg_ids, dbg_w, nullptr,
                     nullptr, stream);
+}
+
+size_t moe_noalloc_workspace_limit(void) { return kNoAllocBytes; }
+
+int32_t moe_layer_forward_noalloc(const moe_layer_desc* L, const uint16_t* x, int32_t T,
+                                  uint16_t* out, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || out == nullptr || !aligned(x, 16) || !aligned(out, 16))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = plan(L, T).total;
+  if (need > kNoAllocBytes) {
+    g_last_error = "moe_layer_forward_noalloc: the layer needs more workspace than the fixed array";
+    return MOE_ERR_WORKSPACE;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      g_scratch_addr[dev] = p;
+    }
+    ws = g_scratch_addr[dev];
+  }
+  return layer_impl(L, x, T, out, ws, kNoAllocBytes, MOE_ACT_EXACT, nullptr, nullptr, nullptr,
+                    nullptr, nullptr, stream);
 }
 
 int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int32_t T,

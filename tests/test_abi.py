@@ -117,6 +117,21 @@ def test_entry_points_reject_before_any_launch():
     assert moe.moe_expert_gemm(0, L, 1, None, None, None, 4, FAKE, FAKE, None, 0, check=False) == -1
 
 
+def test_noalloc_entry_point_rejects_sizes_beyond_its_array():
+    """moe_layer_forward_noalloc: host-side checks only (no GPU here); a T
+    whose workspace exceeds the fixed array is refused before any HIP call."""
+    L = layer()
+    limit = moe.moe_noalloc_workspace_limit()
+    assert limit == 32 << 20
+    T_big = 1
+    while moe.moe_workspace_size(L, T_big) <= limit:
+        T_big *= 2
+    assert moe.moe_layer_forward_noalloc(L, FAKE, T_big, FAKE, check=False) == moe.MOE_ERR_WORKSPACE
+    assert moe.moe_layer_forward_noalloc(L, None, 0, None, check=False) == moe.MOE_OK
+    assert moe.moe_layer_forward_noalloc(L, FAKE + 2, 4, FAKE, check=False) == moe.MOE_ERR_INVALID_ARG
+    assert moe.moe_layer_forward_noalloc(L, FAKE, -1, FAKE, check=False) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     import importlib
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libmoe.so"))
