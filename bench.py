@@ -7,15 +7,19 @@ sets (byte copies at distinct addresses) so each step streams its weights
 from HBM rather than from the last-level cache.  Steps are replayed from a
 captured HIP graph; inputs are resident in HBM before the timed region.
 
-Prints one JSON line.  `value` is tokens/s over the timed steps.  The
-`roofline` object covers the dominant kernel (the routed gate/up expert
-kernel): algorithmic bytes (decode, HBM-bound) or flops (prefill, MFMA-bound)
-per launch over its average launch duration, measured with one pair of HIP
-events around a batch of back-to-back launches on the launch stream;
+Prints one JSON line.  `value` is tokens/s over the timed steps, with
+p10/p50/p90 microseconds per layer over the graph replays.  The `roofline`
+object covers the dominant kernel, the gate/up kernel the layer runs (for
+T <= 8 the decode lowering's gate/up launch, routed and shared experts; the
+expert GEMV up to 64 rows; the grouped GEMM above): algorithmic bytes
+(decode, HBM-bound) or flops (prefill, MFMA-bound) per launch over its
+average launch duration, measured with one pair of HIP events around a batch
+of back-to-back launches on the launch stream;
 `traffic` is the counter-measured HBM bytes per launch from
 profiles/traffic_<workload>.json when those counters were taken on the
 current kernel sources (null otherwise).  The
-`cpu_baseline` object times the CPU oracle on a bounded sample.
+`cpu_baseline` object times the CPU oracle on a bounded sample, at the BLAS
+thread count and at one thread, and names the host CPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -37,6 +41,7 @@ BF16_PEAK_TFLOPS = 2500.0
 FP4_PEAK_TFLOPS = 10100.0
 FP8_PEAK_TFLOPS = 5000.0
 GEMV_MAX_ROWS = 64  # calls with more tokens run the tiled grouped GEMM
+DECODE_ROWS = 8     # calls with at most this many tokens run the decode lowering
 
 # Opt-in lossy activation modes: (C code, arithmetic type, dense MFMA peak of
 # the operand pair in TFLOP/s).  An E4M3 x E2M1 pair runs at the FP8 rate.
@@ -187,13 +192,22 @@ def main():
 
     run_steps(warmup)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    run_steps(steps)
-    ev1.record()
+    # one event before the first replay and one after each: the first to the
+    # last is the timed region; consecutive pairs give each replay's
+    # per-layer time for the percentiles
+    nrep, rem_steps = divmod(steps, per_graph)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 2)]
+    evs[0].record()
+    for i in range(nrep):
+        g_full.replay()
+        evs[i + 1].record()
+    if rem_steps:
+        (g_rem if rem_steps == rem else capture(rem_steps)).replay()
+    evs[-1].record()
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
+    ms = evs[0].elapsed_time(evs[-1])
+    per_layer = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 / per_graph for i in range(nrep))
+    pct = {q: round(float(np.percentile(per_layer, q)), 3) for q in (10, 50, 90)} if per_layer else {}
     wall_s = ms / 1e3
     us_per_layer = ms * 1e3 / steps
     tokens_per_s = steps * T / wall_s
@@ -202,14 +216,14 @@ def main():
     layer_gbs = alg_bytes / (us_per_layer * 1e-6) / 1e9
     layer_tflops = flops / (us_per_layer * 1e-6) / 1e12
     log(f"[bench] {steps} steps: {us_per_layer:.2f} us/layer, {tokens_per_s:.1f} tokens/s, "
-        f"{layer_gbs:.0f} GB/s algorithmic")
+        f"{layer_gbs:.0f} GB/s algorithmic; p10/p50/p90 {pct.get(10)}/{pct.get(50)}/{pct.get(90)} us")
 
     # ---- dominant kernel: routed gate/up expert kernel, timed per launch ----
     E, k = L.E, L.top_k
     P = T * k
     offsets, p2, act, h = dominant_inputs(moe, torch, dev, L, ids)
     M = args.kernel_launches
-    launch_gate_up = dominant_launcher(moe, torch, dev, L, T, x, offsets, p2, act, h, ws,
+    launch_gate_up = dominant_launcher(moe, torch, dev, L, T, x, ids, offsets, p2, act, h, ws,
                                        mode_code if lossy else 0)
     for i in range(min(M, 2 * nsets)):  # warm
         launch_gate_up(sets[i % nsets])
@@ -229,6 +243,9 @@ def main():
     k_avg_us = k0.elapsed_time(k1) * 1e3 / M
     active = np.unique(ids_np)
     k_bytes = len(active) * (expert_bytes(L.gate) + expert_bytes(L.up)) + T * L.H * 2 + P * L.I * 2
+    if T <= DECODE_ROWS and L.has_shared:
+        # the decode gate/up launch computes the shared expert's gate/up too
+        k_bytes += expert_bytes(L.sh_gate) + expert_bytes(L.sh_up) + T * L.I_shared * 2
     k_gbs = k_bytes / (k_avg_us * 1e-6) / 1e9
     k_flops = 2 * P * 2 * L.I * L.H
     k_tflops = k_flops / (k_avg_us * 1e-6) / 1e12
@@ -237,7 +254,9 @@ def main():
         f"{k_tflops:.1f} TFLOP/s")
     if T <= GEMV_MAX_ROWS:
         # weights streamed once per group: bound by HBM
-        roof = {"kernel": dominant_kernel_name(w, mode) + " (routed gate/up + SwiGLU)",
+        what = (" (routed and shared gate/up + SwiGLU)" if T <= DECODE_ROWS and L.has_shared
+                else " (routed gate/up + SwiGLU)")
+        roof = {"kernel": dominant_kernel_name(w, mode) + what,
                 "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                 "avg_launch_us": round(k_avg_us, 3), "algorithmic_bytes_per_launch": k_bytes}
@@ -276,6 +295,9 @@ def main():
             "parallelism": "single-gpu", "act_mode": mode if lossy else "exact",
         },
         "us_per_layer": round(us_per_layer, 3),
+        "us_per_layer_p10_p50_p90": [pct.get(10), pct.get(50), pct.get(90)],
+        "percentiles_over": (f"{nrep} replays of a graph of {per_graph} layer calls "
+                             "(per-layer mean within each replay)"),
         "layer_algorithmic_bytes": alg_bytes,
         "layer_hbm_gbs": round(layer_gbs, 1),
         "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
@@ -310,9 +332,16 @@ def dominant_inputs(moe, torch, dev, L, ids):
     return offsets, p2, act, h
 
 
-def dominant_launcher(moe, torch, dev, L, T, x, offsets, p2, act, h, ws, mode_code):
-    """A function launching the routed gate/up kernel on one weight set: the
-    exact chain's, or (lossy mode) the scaled-MFMA one on x quantized once."""
+def dominant_launcher(moe, torch, dev, L, T, x, ids, offsets, p2, act, h, ws, mode_code):
+    """A function launching the gate/up kernel the layer runs, on one weight
+    set: the decode lowering's (T <= 8: routed and shared experts, on the
+    layer's routing), the expert GEMV or grouped GEMM's, or (lossy mode) the
+    scaled-MFMA one on x quantized once."""
+    if T <= DECODE_ROWS and mode_code == 0:
+        hp = torch.empty((T * L.top_k, L.I), dtype=torch.bfloat16, device=dev)
+        hs = (torch.empty((T, L.I_shared), dtype=torch.bfloat16, device=dev)
+              if L.has_shared else None)
+        return lambda s: moe.moe_decode_gate_up(s.desc, x, T, ids, hp, hs)
     if mode_code == 0:
         return lambda s: moe.moe_expert_gemm(moe.MOE_OP_GATE_UP_SWIGLU, s.desc, 0, offsets, p2,
                                              act, T, x, h, ws)
@@ -337,7 +366,8 @@ def pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws, mode_code):
     the dominant kernel, cycling weight sets as the timed run does."""
     T = ids.shape[0]
     offsets, p2, act, h = dominant_inputs(moe, torch, dev, L, ids)
-    launch_gate_up = dominant_launcher(moe, torch, dev, L, T, x, offsets, p2, act, h, ws, mode_code)
+    launch_gate_up = dominant_launcher(moe, torch, dev, L, T, x, ids, offsets, p2, act, h, ws,
+                                       mode_code)
     src = torch.ones(PMC_COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(PMC_COPIES):  # an elementwise kernel that reads and writes every byte once
@@ -356,7 +386,11 @@ def dominant_kernel_name(w, mode="exact"):
         # K = H a multiple of 128: the LDS-DMA variant (whole K steps)
         base = "grouped_gemm_qd_kernel" if w.H % 128 == 0 else "grouped_gemm_q_kernel"
         return f"{base}<{ACT_MODES[mode][0]}, 0>"
-    fmt = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3, "mxfp8": 4}[w.fmt]
+    codes = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3, "mxfp8": 4}
+    fmt = codes[w.fmt]
+    if w.T <= DECODE_ROWS:
+        sfmt = codes[w.shared_fmt] if w.I_shared else 0
+        return f"decode_gateup_kernel<{fmt}, {sfmt}>"
     if w.T <= GEMV_MAX_ROWS:
         base = "expert_gemv_kernel"
     elif w.fmt in ("nvfp4", "mxfp4") and w.H % 64 == 0:
@@ -369,7 +403,9 @@ def dominant_kernel_name(w, mode="exact"):
 def dominant_sources(T, mode="exact"):
     pkg = os.path.join(ROOT, "quantized_moe_expert_02_amd", "csrc")
     files = ["moe_device.cuh", "gemv_core.cuh"]
-    if T <= GEMV_MAX_ROWS:
+    if T <= DECODE_ROWS:
+        files += ["decode.hip"]
+    elif T <= GEMV_MAX_ROWS:
         files += ["expert_gemv.hip"]
     else:
         files += ["expert_gemm.hip", "expert_gemm_d.hip"] if mode == "exact" else ["expert_gemm_q.hip"]
@@ -444,14 +480,35 @@ def pmc_summarize(workload, mode, fetch_dir, write_dir):
     print(json.dumps(res))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, L, x_bits, budget_s, mode=None):
+    """The oracle on the host's cores, at the BLAS library's full thread count
+    (the reported value) and again limited to one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    res = _cpu_run(w, L, x_bits, budget_s, mode)
+    with threadpool_limits(limits=1):
+        one = _cpu_run(w, L, x_bits, budget_s, mode)
+    res.update({"cores": int(cores), "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+                "value_1thread": one["value"], "seconds_1thread": one["seconds"],
+                "calls_1thread": one["calls"]})
+    return res
+
+
+def _cpu_run(w, L, x_bits, budget_s, mode=None):
     from oracle import layer as O
     from oracle import lossy as Q
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     T = x_bits.shape[0]
     if T <= 64:
         tokens = None
@@ -476,8 +533,8 @@ def cpu_baseline(w, L, x_bits, budget_s, mode=None):
         el = time.time() - t0
         if el >= budget_s or (tokens is not None):
             break
-    return {"value": round(done * per / el, 4), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle", "sample": sample, "seconds": round(el, 2), "calls": done}
+    return {"value": round(done * per / el, 4), "unit": "tokens/s", "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2), "calls": done}
 
 
 if __name__ == "__main__":

@@ -294,6 +294,21 @@ int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int
                                  const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                                  void* ws, size_t ws_bytes, int32_t act_mode, void* stream);
 
+/* The decode lowering's gate/up stage alone (T <= 8), on a given routing:
+ * each active routed expert's gate and up projections streamed once for all
+ * of its tokens, both in one pass with SwiGLU in the epilogue (the pages pair
+ * gate and up in one launch: gitee "dgpp" README, "Execution and
+ * performance", engine.expert_gemm_pair), and the shared expert's.
+ *   topk_ids int32 [T][k] (ids outside [0, E) are skipped);
+ *   h        bf16 [T*k][I]: row t*k+j = bf16(silu(x_t.Wg_e^T) * (x_t.Wu_e^T)),
+ *            e = topk_ids[t][j] (rows of skipped pairs are not written);
+ *   h_shared bf16 [T][I_shared] (the shared expert), NULL without one.
+ * T > 8 returns MOE_ERR_UNSUPPORTED.  This is the first of the decode
+ * lowering's two expert launches, exposed so that it can be timed and
+ * checked on its own; moe_layer_forward runs it for T <= 8. */
+int32_t moe_decode_gate_up(const moe_layer_desc* L, const uint16_t* x, int32_t T,
+                           const int32_t* topk_ids, uint16_t* h, uint16_t* h_shared, void* stream);
+
 /* ---- the layer without a caller workspace ------------------------------
  * For callers that cannot allocate device memory: code under HIP graph
  * capture that must not call hipMalloc, tight serving loops, harnesses that

@@ -13,6 +13,7 @@ import importlib
 _EXPORTS = ("MOE_ACT_EXACT", "MOE_ACT_FP8_T128", "MOE_ACT_MXFP4", "MOE_ACT_MXFP8",
             "moe_expert_gemm_q", "moe_layer_forward_ex", "moe_quantize_act", "moe_route_table",
             "moe_layer_forward_routed", "moe_layer_forward_noalloc", "moe_noalloc_workspace_limit",
+            "moe_decode_gate_up",
             "MOE_ERR_HIP", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
             "MOE_FMT_FP8_B128", "MOE_FMT_MXFP4", "MOE_FMT_MXFP8", "MOE_FMT_NVFP4", "MOE_OK", "MOE_OP_DOWN",
             "MOE_OP_GATE_UP_SWIGLU", "LIB_PATH", "MoeError", "moe_abi_version", "moe_combine",

@@ -37,7 +37,7 @@ EXPORTED = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_valid
             "moe_route_topk", "moe_permute_workspace_size", "moe_permute", "moe_expert_gemm",
             "moe_combine", "moe_layer_forward", "moe_quantize_act", "moe_expert_gemm_q",
             "moe_layer_forward_ex", "moe_route_table", "moe_layer_forward_routed",
-            "moe_noalloc_workspace_limit", "moe_layer_forward_noalloc"]
+            "moe_noalloc_workspace_limit", "moe_layer_forward_noalloc", "moe_decode_gate_up"]
 
 
 class MoeError(RuntimeError):
@@ -93,6 +93,7 @@ def _load():
         "moe_layer_forward_routed": (I32, [LP, P, I32, P, P, P, P, SZ, I32, P]),
         "moe_noalloc_workspace_limit": (SZ, []),
         "moe_layer_forward_noalloc": (I32, [LP, P, I32, P, P]),
+        "moe_decode_gate_up": (I32, [LP, P, I32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -230,3 +231,9 @@ def moe_noalloc_workspace_limit() -> int:
 def moe_layer_forward_noalloc(L, x, T, out, stream=None, check=True):
     st = LIB.moe_layer_forward_noalloc(ctypes.byref(L), _p(x), T, _p(out), _stream(stream))
     return _check(st, "moe_layer_forward_noalloc") if check else st
+
+
+def moe_decode_gate_up(L, x, T, topk_ids, h, h_shared, stream=None, check=True):
+    st = LIB.moe_decode_gate_up(ctypes.byref(L), _p(x), T, _p(topk_ids), _p(h), _p(h_shared),
+                                _stream(stream))
+    return _check(st, "moe_decode_gate_up") if check else st

@@ -431,6 +431,10 @@ hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s) {
   return launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
 }
 
+hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s) {
+  return by_formats<GateUpLaunch>(a.gate.fmt, a.has_shared ? a.sg.fmt : 0, a, s);
+}
+
 hipError_t launch_decode_experts(const DecodeArgs& a, hipStream_t s) {
   hipError_t err = by_formats<GateUpLaunch>(a.gate.fmt, a.has_shared ? a.sg.fmt : 0, a, s);
   if (err != hipSuccess) return err;

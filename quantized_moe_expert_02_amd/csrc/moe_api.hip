@@ -394,6 +394,35 @@ int32_t run_experts_q(int32_t mode, int op, const moe_layer_desc* L, int shared,
                                           max_tiles, codes, scales, out, s));
 }
 
+// The decode lowering's arguments for (L, T) without its buffers.
+DecodeArgs decode_args(const moe_layer_desc* L, const uint16_t* x, int T, const WsPlan& p) {
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.T = T;
+  a.H = L->H;
+  a.I = L->I;
+  a.E = L->E;
+  a.k = L->top_k;
+  a.renorm = L->renormalize;
+  a.I_shared = L->has_shared ? L->I_shared : 0;
+  a.has_shared = L->has_shared;
+  a.max_groups = p.P < L->E ? p.P : L->E;
+  a.wr = L->router_w;
+  a.bias = L->router_bias;
+  a.gate = wdesc(L->gate);
+  a.up = wdesc(L->up);
+  a.down = wdesc(L->down);
+  if (L->has_shared) {
+    a.sg = wdesc(L->sh_gate);
+    a.su = wdesc(L->sh_up);
+    a.sd = wdesc(L->sh_down);
+  }
+  a.RS = p.dp.RS;
+  a.CS = p.dp.CS;
+  return a;
+}
+
 // The layer.  given_ids / given_w: a routing to use instead of the router
 // (moe_layer_forward_routed), else nullptr.
 int32_t layer_impl(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out, void* ws,
@@ -428,30 +457,7 @@ int32_t layer_impl(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16
   int* ids = routed ? const_cast<int*>(given_ids) : (dbg_ids ? dbg_ids : at<int>(ws, p.ids));
   float* w = routed ? const_cast<float*>(given_w) : (dbg_w ? dbg_w : at<float>(ws, p.w));
   if (T <= kDecodeRows) {
-    DecodeArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.x = x;
-    a.T = T;
-    a.H = L->H;
-    a.I = L->I;
-    a.E = L->E;
-    a.k = L->top_k;
-    a.renorm = L->renormalize;
-    a.I_shared = L->has_shared ? L->I_shared : 0;
-    a.has_shared = L->has_shared;
-    a.max_groups = p.P < L->E ? p.P : L->E;
-    a.wr = L->router_w;
-    a.bias = L->router_bias;
-    a.gate = wdesc(L->gate);
-    a.up = wdesc(L->up);
-    a.down = wdesc(L->down);
-    if (L->has_shared) {
-      a.sg = wdesc(L->sh_gate);
-      a.su = wdesc(L->sh_up);
-      a.sd = wdesc(L->sh_down);
-    }
-    a.RS = p.dp.RS;
-    a.CS = p.dp.CS;
+    DecodeArgs a = decode_args(L, x, T, p);
     a.part = at<float>(ws, p.dpart);
     a.apart = at<float>(ws, p.dapart);
     a.logits_out = dbg_logits;
@@ -636,6 +642,25 @@ int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T,
                           float* dbg_w, void* stream) {
   return layer_impl(L, x, T, out, ws, ws_bytes, MOE_ACT_EXACT, dbg_logits, dbg_ids, dbg_w, nullptr,
                     nullptr, stream);
+}
+
+int32_t moe_decode_gate_up(const moe_layer_desc* L, const uint16_t* x, int32_t T,
+                           const int32_t* topk_ids, uint16_t* h, uint16_t* h_shared, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > kDecodeRows) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || topk_ids == nullptr || h == nullptr || !aligned(x, 16) || !aligned(h, 16) ||
+      !aligned(topk_ids, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (L->has_shared && (h_shared == nullptr || !aligned(h_shared, 16))) return MOE_ERR_INVALID_ARG;
+  const WsPlan p = plan(L, T);
+  DecodeArgs a = decode_args(L, x, T, p);
+  a.ids = const_cast<int32_t*>(topk_ids);  // only read
+  a.h = h;
+  a.hs = L->has_shared ? h_shared : nullptr;
+  return hip_status(launch_decode_gate_up(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_noalloc_workspace_limit(void) { return kNoAllocBytes; }

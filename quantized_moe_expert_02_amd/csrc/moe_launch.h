@@ -169,6 +169,9 @@ hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s);
 // The fused decode's expert launches alone (gate/up + SwiGLU, down + combine)
 // on the routing in a.ids / a.w.
 hipError_t launch_decode_experts(const DecodeArgs& a, hipStream_t s);
+// Its first launch alone: routed gate/up + SwiGLU into a.h (row t*k+j) and
+// the shared expert's into a.hs, on the routing in a.ids.
+hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s);
 // Token-table routing on given logits [T][E] (k <= 64).
 hipError_t launch_table_route(const int* tok, const int* table, int V, int T, int k, int E,
                               const float* logits, int renorm, int* ids, float* w, hipStream_t s);

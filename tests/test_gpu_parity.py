@@ -436,6 +436,28 @@ def test_expert_gemm_and_combine_units(name):
     assert_close(O.bf16_value(bf16_bits(out)), ref.out, name + " combine")
 
 
+@pytest.mark.parametrize("name", ["nvfp4_ragged", "mxfp4_ragged", "fp8_ragged", "nvfp4_t3_k1",
+                                  "decode_t1_nvfp4", "decode_t8_mxfp4_zipf"])
+def test_decode_gate_up_unit(name):
+    """moe_decode_gate_up (the decode lowering's gate/up launch, timed by the
+    bench) on the oracle's routing: every routed h row and the shared h."""
+    w = SMALL.get(name) or W[name]
+    L = layer_for(w)
+    x_bits = synth.make_x(w)[:min(w.T, 8)]
+    T, k, I = x_bits.shape[0], w.top_k, w.I
+    say(f"[gpu] decode gate/up unit {name}: T={T} H={w.H} I={I} k={k} fmt={w.fmt}")
+    ref = O.layer_forward(L, x_bits)
+    dl = device_layer(L)
+    ids = torch.from_numpy(ref.routing.ids).cuda()
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
+    hs = torch.empty((T, w.I_shared), dtype=torch.bfloat16, device="cuda") if L.has_shared else None
+    moe.moe_decode_gate_up(dl.desc, bf16_tensor(x_bits), T, ids, h, hs)
+    torch.cuda.synchronize()
+    assert_close(O.bf16_value(bf16_bits(h)), ref.h.reshape(T * k, I), name + " decode h")
+    if L.has_shared:
+        assert_close(O.bf16_value(bf16_bits(hs)), ref.h_shared, name + " decode shared h")
+
+
 def test_workspace_reuse_across_batch_sizes():
     """One zero-filled workspace, calls with T = 8, 1, 5, 8 in a row: the fused
     decode kernels leave their counters zero, so every call stays exact."""
