@@ -219,6 +219,119 @@ __device__ inline bool derive_group(const DecodeArgs& a, int q, GroupSmem& g, in
 
 constexpr int kGuWK = GemvShape<kOpGateUp>::WK;  // K split of the gate/up tiles
 
+// ---- aligned FP4 gate/up tile (the common checkpoint layout) ---------------
+// For FP4 experts whose K (= H) is a multiple of 2048 with whole-chunk scale
+// words (WDesc::wide), a 16-row tile of gate and up is computed with no
+// per-load bounds test: wavefront w takes the contiguous K quarter
+// [w K/4, (w+1) K/4) in whole batches of four 128-K chunks, every lane's loads of a
+// batch share one base address per matrix (immediate offsets), the group's
+// input rows (at most 8 tokens) are staged once in LDS and read from there
+// as the MFMA B operand, and the four quarters are summed in a fixed order.
+constexpr int kLeanMaxRows = kTmax;
+constexpr int kLeanMaxK = 4096;
+
+struct LeanSmem {
+  f32x4 red[kGuWK][2][kWave];
+  ScaleXchg sx[kGuWK][2];
+  __attribute__((aligned(16))) uint16_t x[kLeanMaxRows * kLeanMaxK];
+};
+
+// K quarters made of whole four-chunk batches: every load of a wavefront
+// stays inside its own quarter of the row.
+constexpr int kLeanKStep = 128 * 4 * kGuWK;
+
+__host__ __device__ __forceinline__ bool lean_fits(const DecodeArgs& a) {
+  return a.gate.wide && a.up.wide && a.H % kLeanKStep == 0 && a.H <= kLeanMaxK;
+}
+
+template <int FMT>
+__device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const int* toks,
+                                    const int* pairs, int tile, LeanSmem& sm) {
+  static_assert(FMT == FMT_NVFP4 || FMT == FMT_MXFP4, "FP4 layouts");
+  const int H = a.H, I = a.I;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int r = lane & 15, g = lane >> 4;
+  // the group's input rows into LDS (16-byte pieces, every thread)
+  for (int i = threadIdx.x * 8; i < nrows * H; i += kWave * kGuWK * 8) {
+    const int row = i / H, k = i - row * H;
+    *reinterpret_cast<u32x4*>(&sm.x[i]) =
+        *reinterpret_cast<const u32x4*>(a.x + (size_t)toks[row] * H + k);
+  }
+  const int n0 = tile * 16;
+  const int rb = H / 2;  // code bytes per row
+  const int spw = H / (128 * kGuWK);  // chunks per wavefront
+  const int c0 = wave * spw;
+  const uint8_t* gq = a.gate.codes + e * a.gate.stride_codes + (size_t)(n0 + r) * rb + 16 * g;
+  const uint8_t* uq = a.up.codes + e * a.up.stride_codes + (size_t)(n0 + r) * rb + 16 * g;
+  const uint8_t* gs = scale_row_ptr<FMT>(a.gate, e, n0 + r);
+  const uint8_t* us = scale_row_ptr<FMT>(a.up, e, n0 + r);
+  float tsg = 1.0f, tsu = 1.0f;
+  if constexpr (FMT == FMT_NVFP4) {
+    tsg = a.gate.tscale[e];
+    tsu = a.up.tscale[e];
+  }
+  __syncthreads();  // x staged
+  f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
+  const uint16_t* xr = (r < nrows) ? sm.x + r * H : nullptr;
+  for (int cb = c0; cb < c0 + spw; cb += 4) {
+    ARaw<FMT> pg[4], pu[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      pg[d].q = *reinterpret_cast<const u32x4*>(gq + 64 * (cb + d));
+      pu[d].q = *reinterpret_cast<const u32x4*>(uq + 64 * (cb + d));
+    }
+    uint2 swg, swu;
+    if constexpr (FMT == FMT_NVFP4) {
+      swg = *reinterpret_cast<const uint2*>(gs + 8 * (cb + g));
+      swu = *reinterpret_cast<const uint2*>(us + 8 * (cb + g));
+    } else {
+      swg = make_uint2(*reinterpret_cast<const uint32_t*>(gs + 4 * (cb + g)), 0u);
+      swu = make_uint2(*reinterpret_cast<const uint32_t*>(us + 4 * (cb + g)), 0u);
+    }
+    const uint2 og = exchange_scales<FMT>(swg, sm.sx[wave][0], r, g);
+    const uint2 ou = exchange_scales<FMT>(swu, sm.sx[wave][1], r, g);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      pg[d].s = scale_of_chunk<FMT>(og, d);
+      pu[d].s = scale_of_chunk<FMT>(ou, d);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      u32x4 bx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bx[i] = xr ? *reinterpret_cast<const u32x4*>(xr + 128 * (cb + d) + 32 * g + 8 * i)
+                   : u32x4{0, 0, 0, 0};
+      ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pg[d]), as_bf16x8(bx[0]), ag, 0, 0, 0);
+      au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pu[d]), as_bf16x8(bx[0]), au, 0, 0, 0);
+      ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pg[d]), as_bf16x8(bx[1]), ag, 0, 0, 0);
+      au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pu[d]), as_bf16x8(bx[1]), au, 0, 0, 0);
+      ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pg[d]), as_bf16x8(bx[2]), ag, 0, 0, 0);
+      au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pu[d]), as_bf16x8(bx[2]), au, 0, 0, 0);
+      ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pg[d]), as_bf16x8(bx[3]), ag, 0, 0, 0);
+      au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pu[d]), as_bf16x8(bx[3]), au, 0, 0, 0);
+    }
+  }
+  // the four K quarters, summed in order
+  sm.red[wave][0][lane] = ag;
+  sm.red[wave][1][lane] = au;
+  __syncthreads();
+  if (wave != 0 || r >= nrows) return;
+  f32x4 sg = sm.red[0][0][lane], su = sm.red[0][1][lane];
+#pragma unroll
+  for (int w = 1; w < kGuWK; ++w) {
+    sg = sg + sm.red[w][0][lane];
+    su = su + sm.red[w][1][lane];
+  }
+  // lane (r, g): rows n0 + 4g + j of group row r
+  uint16_t hv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) hv[j] = f32_to_bf16(silu_fast(sg[j] * tsg) * (su[j] * tsu));
+  uint16_t* o = a.h + (size_t)pairs[r] * I + n0 + 4 * g;
+  *reinterpret_cast<uint2*>(o) =
+      make_uint2(hv[0] | (uint32_t(hv[1]) << 16), hv[2] | (uint32_t(hv[3]) << 16));
+}
+
 template <int RFMT, int SFMT>
 __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs a) {
   __shared__ GemvSmem<1, kGuWK, 2> sm;
@@ -238,6 +351,13 @@ __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs
   const int q = b / ntiles, tile = b % ntiles;
   int e, n;
   if (!derive_group(a, q, grp, e, n)) return;
+  if constexpr (RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4) {
+    if (lean_fits(a)) {
+      extern __shared__ __attribute__((aligned(16))) char lean_dyn[];
+      gate_up_lean<RFMT>(a, e, n, grp.toks, grp.pairs, tile, *reinterpret_cast<LeanSmem*>(lean_dyn));
+      return;
+    }
+  }
   GemvIO io{a.x, a.h, nullptr, a.k, kInList, a.T};
   gemv_tile<RFMT, kOpGateUp, 1, kGuWK>(a.gate, a.up, io, GemvRows{e, 0, n, grp.toks, grp.pairs},
                                        tile, sm);
@@ -370,7 +490,10 @@ struct GateUpLaunch {
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
     const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
     const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
-    return launch(decode_gateup_kernel<RFMT, SFMT>, dim3(nsg + ngu), dim3(kWave * kGuWK), 0, s,
+    // the aligned FP4 tile's LDS: reductions, scale exchange, T input rows
+    const bool lean = (RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4) && lean_fits(a);
+    const size_t dyn = lean ? offsetof(LeanSmem, x) + (size_t)a.T * a.H * 2 : 0;
+    return launch(decode_gateup_kernel<RFMT, SFMT>, dim3(nsg + ngu), dim3(kWave * kGuWK), dyn, s,
                   a);
   }
 };

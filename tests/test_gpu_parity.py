@@ -40,6 +40,13 @@ SMALL = {
     "mxfp4_aligned": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp4_aligned", T=11, H=768, E=10,
                                   I=256, top_k=2, fmt=synth.FMT_MXFP4, I_shared=256,
                                   shared_fmt=synth.FMT_MXFP4, zipf_s=1.1),
+    # K a multiple of 2048: the decode's aligned FP4 gate/up tile (K quarters
+    # of one and of two four-chunk batches)
+    "nvfp4_k2048": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_k2048", T=6, H=2048, E=12, I=256,
+                                top_k=3, I_shared=128, shared_fmt=synth.FMT_NVFP4, zipf_s=1.1),
+    "mxfp4_k4096": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp4_k4096", T=8, H=4096, E=10, I=128,
+                                top_k=2, fmt=synth.FMT_MXFP4, I_shared=64,
+                                shared_fmt=synth.FMT_FP8, zipf_s=1.1),
 }
 
 
@@ -534,6 +541,18 @@ def test_degenerate_weights(fmt, T):
     x_bits = synth.make_x(w)[:T]
     say(f"[gpu] degenerate weights fmt={fmt} T={T}")
     r = check_layer_against_oracle(L, x_bits, what=f"degenerate {fmt} T={T}")
+    assert np.isnan(r["out"]).any() and np.isfinite(r["out"]).any()
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_NVFP4, synth.FMT_MXFP4])
+@pytest.mark.parametrize("T", [1, 5])
+def test_degenerate_weights_k2048(fmt, T):
+    """The degenerate values through the decode's aligned FP4 gate/up tile
+    (K = H = 2048)."""
+    w, L = _degenerate_layer(fmt, H=2048, I=256)
+    x_bits = synth.make_x(w)[:T]
+    say(f"[gpu] degenerate weights (K = 2048) fmt={fmt} T={T}")
+    r = check_layer_against_oracle(L, x_bits, what=f"degenerate k2048 {fmt} T={T}")
     assert np.isnan(r["out"]).any() and np.isfinite(r["out"]).any()
 
 
