@@ -33,20 +33,24 @@ constexpr int kTmax = 8;  // decode rows
 constexpr int kPmax = kTmax * kMaxTopK;
 constexpr int kRSBatch = 16;
 
+template <int NT>
 struct RouterSmem {
-  float xs[kTmax][kRH];
-  double red[8][kTmax][kRouterCols];
-  float reda[8][kTmax][kRouterCols];
+  float xs[NT][kRH];
+  double red[8][NT][kRouterCols];
+  float reda[8][NT][kRouterCols];
 };
 
+// NT: tokens per block (1 for a single token, else groups of 8), so that a
+// single-token call carries no per-token guards in its unrolled loops.
+template <int NT>
 __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
-  __shared__ RouterSmem sm;
+  __shared__ RouterSmem<NT> sm;
   const int rb = blockIdx.x;
   const int T = a.T, H = a.H, E = a.E;
   const int cs = rb / a.RS, rs = rb % a.RS;
   // token group: tokens t0 .. t0 + nt - 1 (batches above 8 tokens launch
   // one group of 8 per grid row)
-  const int t0 = blockIdx.y * kTmax, nt = min(kTmax, T - t0);
+  const int t0 = blockIdx.y * NT, nt = min(NT, T - t0);
   const int col = threadIdx.x & 31, rg = threadIdx.x >> 5;
   const int e = cs * kRouterCols + col;
   const int h0 = rs * kRH, nh = min(kRH, H - h0);
@@ -58,15 +62,15 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
     const int h = rg + 8 * j;
     wv[j] = (e < E && h < nh) ? a.wr[(size_t)(h0 + h) * E + e] : 0.f;
   }
-  for (int i = threadIdx.x; i < kTmax * kRH; i += 256) {
+  for (int i = threadIdx.x; i < NT * kRH; i += 256) {
     const int t = i / kRH, h = i % kRH;
     sm.xs[t][h] = (t < nt && h < nh) ? bf16_to_f32(a.x[(size_t)(t0 + t) * H + h0 + h]) : 0.f;
   }
   __syncthreads();
-  double acc[kTmax];
-  float aa[kTmax];
+  double acc[NT];
+  float aa[NT];
 #pragma unroll
-  for (int t = 0; t < kTmax; ++t) {
+  for (int t = 0; t < NT; ++t) {
     acc[t] = 0.0;
     aa[t] = 0.f;
   }
@@ -76,15 +80,15 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
     const double wd = wv[j];
     const float wa = fabsf(wv[j]);
 #pragma unroll
-    for (int t = 0; t < kTmax; ++t) {
-      if (t < nt) {  // bf16 * fp32 is exact in float64
+    for (int t = 0; t < NT; ++t) {
+      if (NT == 1 || t < nt) {  // bf16 * fp32 is exact in float64
         acc[t] = fma(static_cast<double>(sm.xs[t][h]), wd, acc[t]);
         aa[t] = fmaf(fabsf(sm.xs[t][h]), wa, aa[t]);
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < kTmax; ++t) {
+  for (int t = 0; t < NT; ++t) {
     sm.red[rg][t][col] = acc[t];
     sm.reda[rg][t][col] = aa[t];
   }
@@ -105,6 +109,7 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
 __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a) {
   __shared__ double v[kMaxExperts];
   __shared__ WaveTopkScratch wsc;
+  __shared__ BlockFastTopkSmem<kTopkThreads> fsm;
   __shared__ float amax_w[kTopkThreads / kWave];
   const int t = blockIdx.x, T = a.T, E = a.E;
   float amax = 0.f;
@@ -139,18 +144,23 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a)
   amax = wave_max_f(amax);
   if ((threadIdx.x & (kWave - 1)) == 0) amax_w[threadIdx.x / kWave] = amax;
   __syncthreads();
-  // The selection runs on one wavefront (no block barriers): threshold from
-  // the lane maxima, exact ranking of the candidates, certification.
-  if (threadIdx.x >= kWave) return;
   float am = 0.f;
   for (int i = 0; i < (int)(blockDim.x / kWave); ++i) am = fmaxf(am, amax_w[i]);
+  // fast-logit error < 2^-23 * sum|x||w| (covers the fp32 slice roundings)
+  const double bound = static_cast<double>(am) * 0x1p-23;
+  // The whole block selects and certifies; only when that fails (close
+  // gaps, non-finite values, many ties) does one wavefront recompute what
+  // it must.
+  if (block_topk_fast<kTopkThreads>(v, E, a.k, a.renorm, bound, fsm, a.ids + (size_t)t * a.k,
+                                    a.w + (size_t)t * a.k))
+    return;
+  if (threadIdx.x >= kWave) return;
   TopkToken tk;
   tk.vals = v;
   tk.E = E;
   tk.k = a.k;
   tk.renorm = a.renorm;
-  // fast-logit error < 2^-23 * sum|x||w| (covers the fp32 slice roundings)
-  tk.bound = static_cast<double>(am) * 0x1p-23;
+  tk.bound = bound;
   tk.certify = true;
   tk.xrow = a.x + (size_t)t * a.H;
   tk.wr = a.wr;  // [H][E]
@@ -547,9 +557,14 @@ DecodePlan decode_plan(int T, int H, int E) {
   return p;
 }
 
-hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_router(const DecodeArgs& a, hipStream_t s) {
+  if (a.T == 1) return launch(decode_router_kernel<1>, dim3(a.RS * a.CS), dim3(256), 0, s, a);
   const dim3 grid(a.RS * a.CS, (a.T + kTmax - 1) / kTmax);
-  hipError_t err = launch(decode_router_kernel, grid, dim3(256), 0, s, a);
+  return launch(decode_router_kernel<kTmax>, grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s) {
+  hipError_t err = launch_decode_router(a, s);
   if (err != hipSuccess) return err;
   return launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
 }
@@ -565,7 +580,7 @@ hipError_t launch_decode_experts(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  hipError_t err = launch(decode_router_kernel, dim3(a.RS * a.CS), dim3(256), 0, s, a);
+  hipError_t err = launch_decode_router(a, s);
   if (err != hipSuccess) return err;
   err = launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
   if (err != hipSuccess) return err;

@@ -683,6 +683,138 @@ __device__ inline void wave_topk(const TopkToken& a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Certified top-k of one token by a whole workgroup of NTH threads with no
+// serial step per selected expert:
+//   (1) every wavefront finds the (k+1)-th largest 16-bit coarse key among
+//       its lanes' maxima (a 16-step bisection, all wavefronts in parallel);
+//       the largest of those is a lower bound for the overall (k+1)-th
+//       largest coarse key (each wavefront alone holds k+1 keys at or above
+//       its value), so every member of the first k+1 is at or above it;
+//   (2) the candidates at or above it are compacted into LDS (one atomic per
+//       wavefront) and each ranks itself against all of them on the exact
+//       order keys (one thread per candidate, LDS reads in groups of 8);
+//   (3) the first k+1 are certified as in wave_topk.
+// Returns false, with nothing written, when the fast order cannot be
+// certified (close gaps, a non-finite value among the first k+1, more
+// candidates than one wavefront holds) or renormalisation is off: the caller
+// then runs wave_topk, which recomputes what it must.  The coarse key is the
+// top 16 bits of coarse_key (monotone in the logit); a NaN keeps key 1 so
+// that it stays eligible below every number.
+template <int NTH>
+struct BlockFastTopkSmem {
+  uint32_t wthr[NTH / kWave];
+  int ncand;
+  int ok;
+  int cand[kWave];  // reads in groups of 8 stay inside (nc <= 64)
+  uint64_t ckey[kWave];
+  double tv[kMaxTopK + 1];
+  int ti[kMaxTopK + 1];
+};
+
+__device__ __forceinline__ uint32_t coarse16(double v) {
+  const uint32_t c = coarse_key(v, false);
+  return c == 0u ? 0u : max(c >> 16, 1u);
+}
+
+// vals: LDS [E] float64 logits, visible to the block; thread t owns experts
+// t + NTH i.  ids / w: [k] outputs.
+template <int NTH>
+__device__ inline bool block_topk_fast(const double* vals, int E, int k, int renorm, double bound,
+                                       BlockFastTopkSmem<NTH>& sm, int* ids, float* w) {
+  constexpr int kPer = (kMaxExperts + NTH - 1) / NTH;
+  constexpr int kNW = NTH / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int K1 = (k + 1 <= E) ? k + 1 : k;
+  uint32_t c[kPer];
+  uint32_t lm = 0u;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + NTH * i;
+    c[i] = (e < E) ? coarse16(vals[e]) : 0u;
+    lm = max(lm, c[i]);
+  }
+  uint32_t tw = 0u;
+#pragma unroll
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t cand = tw | (1u << bit);
+    if (__popcll(__ballot(lm >= cand)) >= K1) tw = cand;
+  }
+  if (lane == 0) sm.wthr[wave] = tw;
+  if (threadIdx.x == 0) sm.ncand = 0;
+  __syncthreads();
+  uint32_t t = 0u;
+#pragma unroll
+  for (int i = 0; i < kNW; ++i) t = max(t, sm.wthr[i]);
+  if (t == 0u) t = 1u;  // fewer than k+1 eligible in every wavefront: all eligible
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  uint64_t bq[kPer];
+  int nw = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    bq[i] = __ballot(c[i] >= t);
+    nw += __popcll(bq[i]);
+  }
+  int base = 0;
+  if (lane == 0 && nw > 0) base = atomicAdd(&sm.ncand, nw);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int slot = base + __popcll(bq[i] & lt);
+    if (((bq[i] >> lane) & 1ull) && slot < kWave) {
+      const int e = threadIdx.x + NTH * i;
+      sm.cand[slot] = e;
+      sm.ckey[slot] = order_key(vals[e], false);
+    }
+    base += __popcll(bq[i]);
+  }
+  __syncthreads();
+  const int nc = sm.ncand;
+  if (nc > kWave || renorm == 0) return false;  // uniform: every thread read the same nc
+  if ((int)threadIdx.x < nc) {
+    const int e = sm.cand[threadIdx.x];
+    const uint64_t ke = sm.ckey[threadIdx.x];
+    int cnt = 0;
+    for (int j0 = 0; j0 < nc; j0 += 8) {
+      uint64_t kj[8];
+      int ej[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        kj[q] = sm.ckey[j0 + q];
+        ej[q] = sm.cand[j0 + q];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j0 + q < nc) cnt += ranks_before(kj[q], ej[q], ke, e);
+    }
+    if (cnt < K1) {
+      sm.tv[cnt] = (ke == 1ull) ? __builtin_nan("") : vals[e];
+      sm.ti[cnt] = e;
+    }
+  }
+  __syncthreads();
+  const int got = min(K1, nc);
+  if (wave == 0) {
+    const double tv = (lane < got) ? sm.tv[lane] : 0.0;
+    const double nv = __shfl_down(tv, 1, kWave);
+    const bool fin = (lane >= got) || (tv - tv == 0.0);
+    const bool gap = (lane + 1 >= got) || (tv - nv > 2.0 * bound);
+    const bool ok = (got == K1) && __all(fin) && __all(gap);
+    if (ok) {  // weights as wave_topk computes them (renormalised softmax)
+      const double v0 = __shfl(tv, 0, kWave);
+      const float z = (lane < k) ? expf(static_cast<float>(tv - v0)) : 0.f;
+      const float denom = dpp_sum_f(z);
+      if (lane < k) {
+        ids[lane] = sm.ti[lane];
+        w[lane] = z / denom;
+      }
+    }
+    if (lane == 0) sm.ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+  return sm.ok != 0;
+}
+
 // Per-group descriptor the fused decode kernels read in one step.
 constexpr int kGroupDescInts = 20;  // e, p0, nrows, spare, 16 input-token rows
 constexpr int kGroupDescRows = 16;
