@@ -437,7 +437,8 @@ hipError_t launch_fmt(int op, const GemmParams& p, int n_row_tiles, hipStream_t 
 hipError_t launch_grouped_gemm(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
                                const int* tiles, const int* n_tiles, int max_tiles,
                                const uint16_t* in, void* out, hipStream_t s) {
-  if (grouped_gemm_dma_fits(op, w0, w1) && reinterpret_cast<uintptr_t>(in) % 16 == 0)
+  const int dma_rows = (g.shared || op == kOpGateUp) ? g.T : g.T * g.topk;
+  if (grouped_gemm_dma_fits(op, w0, w1, dma_rows) && reinterpret_cast<uintptr_t>(in) % 16 == 0)
     return launch_grouped_gemm_dma(op, w0, w1, g, tiles, n_tiles, max_tiles, in, out, s);
   GemmParams p;
   p.w0 = w0;

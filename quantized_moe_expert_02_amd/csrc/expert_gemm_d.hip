@@ -7,12 +7,12 @@
 // (weights decoded to bf16 exactly: NVFP4 E2M1 x E4M3 block scale, MXFP4
 // E2M1 x E8M0; v_mfma_f32_16x16x32_bf16, K in steps of 64), on tiles of 128
 // permuted rows x 256 weight rows (gate/up: 128 gate + the matching 128 up
-// rows), but:
+// rows), four wavefronts, two workgroups per CU, but:
 //
 // * no staging registers: bf16 activation rows (gathered through
 //   perm_to_pair), the packed E2M1 codes and the block-scale words of a step
-//   are DMA'd into LDS (global_load_lds), two stages, one bare barrier per
-//   step after an explicit vmcnt wait;
+//   are DMA'd into LDS (buffer loads to LDS), three stages, one bare barrier
+//   per step after an explicit vmcnt wait;
 // * the weight tile stays packed in LDS (8 KiB per step instead of 32 KiB of
 //   bf16); on a 1 x 4 wavefront grid (128 rows x 64 weight rows each) a
 //   wavefront reads the 4 bytes (8 codes) and the scale byte of each of its B
@@ -32,8 +32,14 @@ namespace moe {
 namespace {
 
 constexpr int BM = kGemmTileM, BN = 256, BK = 64;
+constexpr int kWaves = 4, kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
-constexpr int kStages = 2;
+// Three stages of 25 KiB: two steps in flight while one is computed; two
+// workgroups per CU still fit the 160 KiB of LDS.
+constexpr int kStages = 3;
+constexpr int kAPerWave = BM * 128 / 1024 / kWaves;  // KiB-chunks of activations per wave and step
+constexpr int kBPerWave = BN * 32 / 1024 / kWaves;   // KiB-chunks of codes per wave and step
+constexpr int kDmaPerStage = kAPerWave + kBPerWave + 1;  // per lane and step (+1: scale words)
 
 template <int FMT>
 struct DLayout {
@@ -47,20 +53,28 @@ struct DLayout {
   static constexpr int s_pitch = 4;                          // LDS bytes per row
   static constexpr int s_bytes = BN * s_pitch;               // one 64-lane region per wave
   static constexpr int stage = s_off + s_bytes;
-  static_assert(BN == 4 * 64, "each wavefront DMAs the scale words of 64 weight rows");
+  static_assert(BN == kWaves * 64, "each wavefront DMAs the scale words of 64 weight rows");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Buffer resource over [base, base + bytes), raw (stride 0) dword access
+// (gfx9 word 3).  The DMA loads below take a per-lane offset fixed for the
+// whole K loop and the step's offset in an SGPR, so a step's loads cost no
+// vector address arithmetic; offsets past `bytes` read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int SIZE>
-__device__ __forceinline__ void dma(const void* src, uint8_t* lds) {
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
   static_assert(SIZE == 2 || SIZE == 4 || SIZE == 16, "LDS-DMA size");
   if constexpr (SIZE == 16)
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, (int)voff, (int)soff, 0, 0);
   else if constexpr (SIZE == 4)
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, (int)voff, (int)soff, 0, 0);
   else
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds, 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 2, (int)voff, (int)soff, 0, 0);
 }
 
 // vmcnt(N) and lgkmcnt(0) (gfx9 encoding).
@@ -79,6 +93,7 @@ struct DParams {
   const int* offsets;
   const int* perm_to_pair;
   int topk, T, in_rows, in_rows_total, max_rt, ntn;
+  uint32_t in_bytes;  // in_rows * K * 2 < 2^31
 };
 
 template <int OP>
@@ -119,18 +134,20 @@ __device__ __forceinline__ bf16x8 decode_frag(uint32_t d, uint32_t sbyte) {
 
 template <int FMT>
 struct DWaves {
-  // 1 x 4 for both formats (measured at T=8192: NVFP4 layer -5..-8%, MXFP4
-  // layer -2..-3% against 2 x 2); the grid stays a parameter.
-  static constexpr int KWM = 1, KWN = 4 / KWM;
+  // 1 x 4: every B fragment is decoded by one wavefront (measured at T=8192:
+  // NVFP4 layer -5..-8%, MXFP4 layer -2..-3% against 2 x 2); the grid stays
+  // a parameter.
+  static constexpr int KWM = 1, KWN = kWaves / KWM;
   static constexpr int R = BM / KWM / 16, C = BN / KWN / 16;
 };
 
 template <int FMT, int OP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_d_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_d_kernel(
     DParams p) {
   using D = DLayout<FMT>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * D::stage];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // wave index in an SGPR: the DMA destinations (M0) are scalar arithmetic
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n_rt = (p.tiles == nullptr) ? (p.T + BM - 1) / BM : min(*p.n_tiles, p.max_rt);
   const int live = n_rt * p.ntn;
   const int per = (live + kXcds - 1) / kXcds;
@@ -154,49 +171,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int n0 = nt * ((OP == kOpGateUp) ? BN / 2 : BN);
   const int nk = K / BK;
 
-  // ---- DMA sources of this lane ----
+  // ---- DMA sources of this lane: byte offsets in buffers fixed per wave ----
   // A: 16 KiB-chunks of 8 rows x 128 B; wave w takes chunks 4w .. 4w+3.
-  const uint16_t* asrc[4];
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(p.in, p.in_bytes);
+  uint32_t aoff[kAPerWave];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (4 * wave + i) * 8 + (lane >> 3);
+  for (int i = 0; i < kAPerWave; ++i) {
+    const int r = (kAPerWave * wave + i) * 8 + (lane >> 3);
     const int piece = (lane & 7) ^ ((r >> 1) & 7);
-    asrc[i] = p.in + (size_t)input_row<OP>(p, m0 + r, m0, m1) * K + 8 * piece;
+    aoff[i] = (uint32_t)input_row<OP>(p, m0 + r, m0, m1) * (uint32_t)(2 * K) + 16 * piece;
   }
-  // B codes: KiB-chunks of 32 rows x 32 B; wave w takes chunks 2w, 2w+1.
-  const uint8_t* bsrc[2];
+  // B codes: KiB-chunks of 32 rows x 32 B; wave w takes chunks 2w, 2w+1 (the
+  // weight rows 64w .. 64w+63), all rows of one matrix (gate/up: waves 0-1
+  // gate rows, waves 2-3 up rows).
+  static_assert(kBPerWave == 2, "a wave's code chunks cover its 64 scale rows");
+  const WDesc& wq = (OP == kOpGateUp && 64 * wave >= BN / 2) ? p.w1 : p.w0;
+  const __amdgpu_buffer_rsrc_t rb = buf_rsrc(wq.codes + e * wq.stride_codes, (uint32_t)N * (K / 2));
+  uint32_t boff[kBPerWave];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kBPerWave; ++i) {
     const int r = 64 * wave + 32 * i + (lane >> 1);
     const int piece = (lane & 1) ^ ((r >> 3) & 1);
-    const WDesc& wq = (OP == kOpGateUp && r >= BN / 2) ? p.w1 : p.w0;
     const int wr0 = (OP == kOpGateUp) ? n0 + (r & (BN / 2 - 1)) : n0 + r;
     const int wr = wr0 < N ? wr0 : N - 1;
-    bsrc[i] = wq.codes + e * wq.stride_codes + (size_t)wr * (K / 2) + 16 * piece;
+    boff[i] = (uint32_t)wr * (K / 2) + 16 * piece;
   }
   // scale words: wave w the weight rows 64w + lane
-  const uint8_t* ssrc;
+  constexpr int kSpr = (FMT == FMT_NVFP4) ? 16 : 32;  // K per scale byte
+  const __amdgpu_buffer_rsrc_t rs =
+      buf_rsrc(reinterpret_cast<const uint8_t*>(wq.scales) + e * wq.stride_scales, (uint32_t)N * (K / kSpr));
+  uint32_t soff;
   {
     const int r = 64 * wave + lane;
-    const WDesc& wq = (OP == kOpGateUp && r >= BN / 2) ? p.w1 : p.w0;
     const int wr0 = (OP == kOpGateUp) ? n0 + (r & (BN / 2 - 1)) : n0 + r;
     const int wr = wr0 < N ? wr0 : N - 1;
-    ssrc = reinterpret_cast<const uint8_t*>(wq.scales) + e * wq.stride_scales +
-           (size_t)wr * (K / (FMT == FMT_NVFP4 ? 16 : 32));
+    soff = (uint32_t)wr * (K / kSpr);
   }
   const int sdst = D::s_off + 64 * D::s_pitch * wave;
 
-  auto issue = [&](int ks) {
-    uint8_t* st = lds + (ks % kStages) * D::stage;
+  // the stage is a compile-time constant so that every LDS address of a step
+  // is a per-lane base plus an immediate offset
+  auto issue = [&](int ks, auto stage_t) {
+    uint8_t* st = lds + decltype(stage_t)::value * D::stage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma<16>(asrc[i] + ks * BK, st + D::a_off + 1024 * (4 * wave + i));
+    for (int i = 0; i < kAPerWave; ++i)
+      dma_buf<16>(ra, aoff[i], ks * BK * 2, st + D::a_off + 1024 * (kAPerWave * wave + i));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma<16>(bsrc[i] + ks * (BK / 2), st + D::b_off + 1024 * (2 * wave + i));
-    dma<D::s_row>(ssrc + ks * D::s_row, st + sdst);
+    for (int i = 0; i < kBPerWave; ++i)
+      dma_buf<16>(rb, boff[i], ks * (BK / 2), st + D::b_off + 1024 * (kBPerWave * wave + i));
+    dma_buf<D::s_row>(rs, soff, ks * D::s_row, st + sdst);
   };
 
-  // Wavefront grid KWM x KWN over the 128 x 128 tile; each wavefront holds R x
-  // C fragments of 16 x 16.  1 x 4 (128 rows x 32 weight rows each): every B
+  // Wavefront grid KWM x KWN over the 128 x 256 tile; each wavefront holds R x
+  // C fragments of 16 x 16.  1 x 4 (128 rows x 64 weight rows each): every B
   // fragment is decoded by one wavefront only (an NVFP4 decode multiplies by
   // the E4M3 scale in fp32 per weight), at the price of reading each A
   // fragment four times from LDS instead of twice on a 2 x 2 grid.  Gate/up:
@@ -222,52 +249,140 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int vr = vrows <= 0 ? 0 : min(R, (vrows + 15) / 16);
   const int g = lane >> 4, lr = lane & 15;
 
-  auto compute = [&](int ks, auto full_t) {
-    constexpr bool FULL = decltype(full_t)::value;
-    const uint8_t* st = lds + (ks % kStages) * D::stage;
+  // Per-lane LDS byte offsets within a stage, for the two 32-K halves h of a
+  // step.  A wavefront's A fragment rows differ by multiples of 16 and its B
+  // fragments start at rows that are multiples of 16, so the XOR swizzles
+  // depend on the lane only and each fragment's offset is a lane base plus a
+  // compile-time constant.  A fragment r: row 16r + lr, K 32h + 8g .. +8; B
+  // fragment c: the 4 code bytes of weight row bcol[c] + lr at K 32h + 8g
+  // and the scale byte of that K.
+  const int wcol = bcol[0];  // bcol[c] = wcol + ccol(c)
+  auto ccol = [](int c) {
+    return (OP == kOpGateUp) ? ((c < C / 2) ? 16 * c : BN / 2 + 16 * (c - C / 2)) : 16 * c;
+  };
+  int a_lane[2], b_lane[2], s_lane[2];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      // B fragments: row bcol[c] + lr, K kk + 8g .. +8: 4 code bytes at byte
-      // 4g of the row's 16-byte piece kk / 32, and the scale byte of that K
-      bf16x8 bfr[C];
+  for (int h = 0; h < 2; ++h) {
+    a_lane[h] = D::a_off + (kWaveRows * wm + lr) * 128 + 16 * ((4 * h + g) ^ ((lr >> 1) & 7));
+    b_lane[h] = D::b_off + (wcol + lr) * 32 + 16 * (h ^ ((lr >> 3) & 1)) + 4 * g;
+    s_lane[h] = D::s_off + (wcol + lr) * D::s_pitch + ((FMT == FMT_NVFP4) ? 2 * h + (g >> 1) : h);
+  }
+
+  // Software pipeline over half-steps.  While the MFMAs of one half run, the
+  // wavefront reads the raw codes and scale bytes of the next half (from the
+  // next step's stage after half 1), reads the next half's A fragments (each
+  // one after the last MFMA on the fragment it replaces) and decodes the next
+  // half's B fragments.  Only the first half of a tile waits for its decode.
+  bf16x8 acur[R], bcur[C], bnxt[C];
+  uint32_t rd[C], rsb[C];  // raw code words and scale bytes of the next half
+  auto read_raw = [&](const uint8_t* st, int h) {
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int row = bcol[c] + lr;
-        const int slot = (kk >> 5) ^ ((row >> 3) & 1);
-        const uint32_t d = *reinterpret_cast<const uint32_t*>(st + D::b_off + row * 32 + 16 * slot + 4 * g);
-        const int sb = (FMT == FMT_NVFP4) ? (kk >> 4) + (g >> 1) : (kk >> 5);
-        const uint32_t sbyte = st[D::s_off + row * D::s_pitch + sb];
-        bfr[c] = decode_frag<FMT>(d, sbyte);
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (!FULL && r >= vr) continue;
-        const int row = kWaveRows * wm + 16 * r + lr;
-        const int slot = ((kk >> 3) + g) ^ ((row >> 1) & 7);
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(st + D::a_off + row * 128 + 16 * slot);
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-          acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[c], acc[r][c], 0, 0, 0);
-      }
+    for (int c = 0; c < C; ++c) {
+      rd[c] = *reinterpret_cast<const uint32_t*>(st + b_lane[h] + ccol(c) * 32);
+      rsb[c] = st[s_lane[h] + ccol(c) * D::s_pitch];
     }
+  };
+  auto read_a = [&](const uint8_t* st, int h, int r) {
+    return *reinterpret_cast<const bf16x8*>(st + a_lane[h] + 2048 * r);
+  };
+  // decode VALU ops per B fragment (NVFP4: E4M3 scale, 4 conversions, 8
+  // multiplies, 4 packs; MXFP4: 4 scaled conversions and the scale shift)
+  constexpr int kDecV = (FMT == FMT_NVFP4) ? 17 : 5;
+  // One half: MFMAs on (acur, bcur); reads of stage `stn`, half hn; bnxt
+  // decoded.  Instruction order: fragment row 0's MFMAs take the 2C raw reads,
+  // every later MFMA but a row's last takes a share of the decode, and each
+  // row's A read follows the row's last MFMA.
+  auto half = [&](const uint8_t* stn, int hn, auto rv_t) {
+    constexpr int RV = decltype(rv_t)::value;
+    read_raw(stn, hn);
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[r], bcur[c], acc[r][c], 0, 0, 0);
+      acur[r] = read_a(stn, hn, r);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      bnxt[c] = decode_frag<FMT>(rd[c], rsb[c]);
+      // pins the decode to this half: without it the compiler sinks the
+      // decode below the step's barrier, next to its first use
+      asm volatile("" : "+v"(bnxt[c]));
+    }
+    static_assert(C == 4, "the instruction order below assumes 4 fragments per row");
+    constexpr int kSlots = 3 * (RV - 1), kV = (C * kDecV + kSlots - 1) / kSlots;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, C, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, C, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int r = 1; r < RV; ++r) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) bcur[c] = bnxt[c];
   };
 
-  // stage 0 up front; at step ks: this wave's loads of stage ks landed (the
-  // next stage's may be in flight) and its LDS reads of step ks-1 done,
-  // barrier, issue step ks+1 into the buffer of step ks-1, compute step ks.
-  auto main_loop = [&](auto full_t) {
-    issue(0);
-    for (int ks = 0; ks < nk; ++ks) {
+  // Stages: steps 0, 1 and 2 are issued up front.  Step ks: its half 0 reads
+  // the last of stage ks (half 1) into registers; then this wave's loads of
+  // step ks+1 landed (those of ks+2 may be in flight, in-order vmcnt) and all
+  // its LDS reads are done, barrier, step ks+3 is issued into the buffer of
+  // step ks, and half 1 reads half 0 of step ks+1 (at the last step: stale
+  // LDS bytes, never used).
+  static_assert(kStages == 3, "the step loop below is unrolled by three");
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  auto step = [&](int ks, auto stage_t, auto rv_t) {
+    constexpr int SC = decltype(stage_t)::value;
+    half(lds + SC * D::stage, 1, rv_t);
+    if (ks + 2 < nk)
+      wait_vm_lds<kDmaPerStage>();
+    else
       wait_vm_lds<0>();
-      __builtin_amdgcn_s_barrier();
-      if (ks + 1 < nk) issue(ks + 1);
-      compute(ks, full_t);
+    __builtin_amdgcn_s_barrier();
+    if (ks + 3 < nk) issue(ks + 3, stage_t);
+    half(lds + ((SC + 1) % kStages) * D::stage, 0, rv_t);
+  };
+  // RV: the 16-row fragment rows multiplied (a partial tile skips the rest)
+  auto main_loop = [&](auto rv_t) {
+    constexpr int RV = decltype(rv_t)::value;
+    issue(0, S0{});
+    if (nk > 1) issue(1, S1{});
+    if (nk > 2) issue(2, S2{});
+    if (nk > 2)
+      wait_vm_lds<2 * kDmaPerStage>();
+    else if (nk > 1)
+      wait_vm_lds<kDmaPerStage>();
+    else
+      wait_vm_lds<0>();
+    __builtin_amdgcn_s_barrier();
+    read_raw(lds, 0);
+#pragma unroll
+    for (int r = 0; r < RV; ++r) acur[r] = read_a(lds, 0, r);
+#pragma unroll
+    for (int c = 0; c < C; ++c) bcur[c] = decode_frag<FMT>(rd[c], rsb[c]);
+    for (int ks = 0; ks < nk; ks += kStages) {
+      step(ks, S0{}, rv_t);
+      if (ks + 1 < nk) step(ks + 1, S1{}, rv_t);
+      if (ks + 2 < nk) step(ks + 2, S2{}, rv_t);
     }
   };
-  if (m1 - m0 >= BM)
-    main_loop(std::true_type{});
+  static_assert(R == 8, "fragment-row classes 8 / 4 / 2");
+  if (vr > 4)
+    main_loop(std::integral_constant<int, 8>{});
+  else if (vr > 2)
+    main_loop(std::integral_constant<int, 4>{});
   else
-    main_loop(std::false_type{});
+    main_loop(std::integral_constant<int, 2>{});
 
   const float ts0 = (FMT == FMT_NVFP4) ? p.w0.tscale[e] : 1.0f;
   const float ts1 = (FMT == FMT_NVFP4) ? p.w1.tscale[e] : 1.0f;
@@ -295,7 +410,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       }
     __syncthreads();
     // thread -> (row tid / TPR + RPP q, 8 columns at 8 * (tid % TPR))
-    constexpr int TPR = HW / 8, RPP = 256 / TPR;
+    constexpr int TPR = HW / 8, RPP = kThreads / TPR;
     const int cb = 8 * (tid % TPR);
     const int n = nt * HW + cb;
 #pragma unroll
@@ -317,10 +432,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     // y tile: BM rows x BN fp32 columns in parts of QR rows; staged rows of
     // BN + 4 floats (the fragment writes of the four 16-lane groups land in
     // distinct banks)
-    constexpr int P = BN + 4, QR = (BN == 256) ? 32 : 64;
+    constexpr int P = BN + 4, QR = 32;
     static_assert(QR * P * 4 <= kStages * D::stage, "staged part of the y tile fits");
     float* st = reinterpret_cast<float*>(lds);
-    constexpr int TPR = BN / 4, RPP = 256 / TPR;
+    constexpr int TPR = BN / 4, RPP = kThreads / TPR;
     const int cb = 4 * (tid % TPR);
     const int n = n0 + cb;
 #pragma unroll
@@ -358,15 +473,19 @@ hipError_t launch_d(DParams p, int n_row_tiles, hipStream_t s) {
   p.max_rt = n_row_tiles;
   const int per = (n_row_tiles * ntn + kXcds - 1) / kXcds;
   if (per == 0) return hipSuccess;
-  return launch(grouped_gemm_d_kernel<FMT, OP>, dim3(per * kXcds), dim3(256), 0, s, p);
+  return launch(grouped_gemm_d_kernel<FMT, OP>, dim3(per * kXcds), dim3(kThreads), 0, s, p);
 }
 
 }  // namespace
 
-bool grouped_gemm_dma_fits(int op, const WDesc& w0, const WDesc& w1) {
+bool grouped_gemm_dma_fits(int op, const WDesc& w0, const WDesc& w1, int in_rows) {
   // FP4 only: the 16-byte code pieces of a step are 64 K of one row.
   const bool fmt_ok = w0.fmt == FMT_MXFP4 || w0.fmt == FMT_NVFP4;
   if (!fmt_ok || w1.fmt != w0.fmt || w0.cols % BK != 0) return false;
+  // buffer offsets are 32-bit: the input rows and one expert's codes below 2 GiB
+  if ((size_t)in_rows * w0.cols * 2 >= (size_t(1) << 31) ||
+      (size_t)w0.rows * w0.cols / 2 >= (size_t(1) << 31))
+    return false;
   // the epilogue stores aligned 16-byte column groups: 8 bf16 of h, 4 fp32 of y
   if (w0.rows % ((op == kOpGateUp) ? 8 : 4) != 0) return false;
   // the scale word of a step (4 bytes NVFP4, 2 bytes MXFP4) is one aligned DMA
@@ -383,7 +502,8 @@ bool grouped_gemm_dma_fits(int op, const WDesc& w0, const WDesc& w1) {
 hipError_t launch_grouped_gemm_dma(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
                                    const int* tiles, const int* n_tiles, int max_tiles,
                                    const uint16_t* in, void* out, hipStream_t s) {
-  if (!grouped_gemm_dma_fits(op, w0, w1)) return hipErrorInvalidValue;
+  const int in_rows = (g.shared || op == kOpGateUp) ? g.T : g.T * g.topk;
+  if (!grouped_gemm_dma_fits(op, w0, w1, in_rows)) return hipErrorInvalidValue;
   DParams p;
   p.w0 = w0;
   p.w1 = w1;
@@ -396,6 +516,7 @@ hipError_t launch_grouped_gemm_dma(int op, const WDesc& w0, const WDesc& w1, con
   p.ntn = 0;
   p.max_rt = 0;
   p.in_rows_total = g.T * g.topk;
+  p.in_bytes = 0;
   int nrt;
   if (g.shared) {
     p.tiles = nullptr;
@@ -408,6 +529,7 @@ hipError_t launch_grouped_gemm_dma(int op, const WDesc& w0, const WDesc& w1, con
     nrt = max_tiles;
     p.in_rows = (op == kOpGateUp) ? g.T : g.T * g.topk;
   }
+  p.in_bytes = (uint32_t)((size_t)p.in_rows * w0.cols * 2);
   const bool gu = op == kOpGateUp;
   if (w0.fmt == FMT_NVFP4)
     return gu ? launch_d<FMT_NVFP4, kOpGateUp>(p, nrt, s) : launch_d<FMT_NVFP4, kOpDown>(p, nrt, s);

@@ -115,8 +115,9 @@ hipError_t launch_grouped_gemm(int op, const WDesc& w0, const WDesc& w1, const G
 // K % 64 == 0, output rows a multiple of 8 (gate/up) or 4 (down) and aligned
 // codes, scale words and activations (`in` 16-byte aligned): operands moved by
 // LDS-DMA, weight fragments decoded per wavefront, the output tile stored
-// through LDS (launch_grouped_gemm takes it when it fits).
-bool grouped_gemm_dma_fits(int op, const WDesc& w0, const WDesc& w1);
+// through LDS (launch_grouped_gemm takes it when it fits; in_rows: the rows of
+// `in`, whose bytes and one expert's codes must stay below 2 GiB).
+bool grouped_gemm_dma_fits(int op, const WDesc& w0, const WDesc& w1, int in_rows);
 hipError_t launch_grouped_gemm_dma(int op, const WDesc& w0, const WDesc& w1, const GroupArgs& g,
                                    const int* tiles, const int* n_tiles, int max_tiles,
                                    const uint16_t* in, void* out, hipStream_t s);
