@@ -34,26 +34,37 @@ namespace {
 constexpr int BM = kGemmTileM, BN = 256, BK = 64;
 constexpr int kWaves = 4, kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
-// Three stages of 25 KiB: two steps in flight while one is computed; two
-// workgroups per CU still fit the 160 KiB of LDS.
+// Three stages of 24 KiB and two 4 KiB scale buffers: two steps in flight
+// while one is computed, and two workgroups per CU fill the 160 KiB of LDS.
 constexpr int kStages = 3;
 constexpr int kAPerWave = BM * 128 / 1024 / kWaves;  // KiB-chunks of activations per wave and step
 constexpr int kBPerWave = BN * 32 / 1024 / kWaves;   // KiB-chunks of codes per wave and step
-constexpr int kDmaPerStage = kAPerWave + kBPerWave + 1;  // per lane and step (+1: scale words)
+// DMA instructions per lane and step when the tile's first 16 RV rows are
+// multiplied: only those activation rows are loaded
+template <int RV>
+constexpr int dma_per_stage() { return RV / 2 + kBPerWave; }
 
 template <int FMT>
 struct DLayout {
+  // a stage: one step's activations and codes
   static constexpr int a_off = 0;                   // [128 rows][128 B] bf16
   static constexpr int b_off = BM * 128;            // [BN rows][32 B] E2M1 codes
-  // Scale words of a step: NVFP4 4 bytes, MXFP4 2 bytes per weight row.  A
-  // DMA of 4 bytes or fewer lands at a 4-byte pitch per lane (M0 + 4 * lane),
-  // so each row has a 4-byte slot whatever the word's size.
-  static constexpr int s_off = b_off + BN * 32;
-  static constexpr int s_row = (FMT == FMT_NVFP4) ? 4 : 2;  // bytes loaded per row
-  static constexpr int s_pitch = 4;                          // LDS bytes per row
-  static constexpr int s_bytes = BN * s_pitch;               // one 64-lane region per wave
-  static constexpr int stage = s_off + s_bytes;
-  static_assert(BN == kWaves * 64, "each wavefront DMAs the scale words of 64 weight rows");
+  static constexpr int stage = b_off + BN * 32;
+  // Block scales arrive in chunks of kSC = 4 steps, in two buffers after the
+  // stages.  A DMA lane moves one step's scale bytes of one row (NVFP4 4,
+  // MXFP4 2: the alignment a scale row has with K % 64 == 0) and lands at a
+  // 4-byte pitch, so a row holds [step][4 B] and one DMA instruction covers
+  // 16 rows, touching one cache line per row where a per-step load would
+  // touch one per lane.
+  static constexpr int s_row = (FMT == FMT_NVFP4) ? 4 : 2;  // scale bytes per row and step
+  static constexpr int kSC = 4;                              // steps per scale chunk
+  static constexpr int kLpr = kSC;                           // DMA lanes per row
+  static constexpr int kRpi = 64 / kLpr;                     // rows per DMA instruction
+  static constexpr int kSpi = 64 / kRpi;                     // instructions per wave and chunk
+  static constexpr int s_off = kStages * stage;              // [2][BN rows][16 B]
+  static constexpr int s_buf = BN * 16;
+  static constexpr int total = s_off + 2 * s_buf;
+  static_assert(BN == kWaves * 64, "each wavefront DMAs the scale chunks of 64 weight rows");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -145,7 +156,7 @@ template <int FMT, int OP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void grouped_gemm_d_kernel(
     DParams p) {
   using D = DLayout<FMT>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * D::stage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[D::total];
   // wave index in an SGPR: the DMA destinations (M0) are scalar arithmetic
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n_rt = (p.tiles == nullptr) ? (p.T + BM - 1) / BM : min(*p.n_tiles, p.max_rt);
@@ -172,15 +183,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int nk = K / BK;
 
   // ---- DMA sources of this lane: byte offsets in buffers fixed per wave ----
-  // A: 16 KiB-chunks of 8 rows x 128 B; wave w takes chunks 4w .. 4w+3.
+  // A: the first 16 RV tile rows (RV = 8, 4 or 2 by the rows the tile holds)
+  // in KiB-chunks of 8 rows x 128 B; wave w takes chunks (RV/2) w ..
+  // (RV/2) w + RV/2 - 1.  Set by main_loop.
   const __amdgpu_buffer_rsrc_t ra = buf_rsrc(p.in, p.in_bytes);
   uint32_t aoff[kAPerWave];
+  auto set_aoff = [&](auto rv_t) {
+    constexpr int NA = decltype(rv_t)::value / 2;
 #pragma unroll
-  for (int i = 0; i < kAPerWave; ++i) {
-    const int r = (kAPerWave * wave + i) * 8 + (lane >> 3);
-    const int piece = (lane & 7) ^ ((r >> 1) & 7);
-    aoff[i] = (uint32_t)input_row<OP>(p, m0 + r, m0, m1) * (uint32_t)(2 * K) + 16 * piece;
-  }
+    for (int i = 0; i < NA; ++i) {
+      const int r = (NA * wave + i) * 8 + (lane >> 3);
+      const int piece = (lane & 7) ^ ((r >> 1) & 7);
+      aoff[i] = (uint32_t)input_row<OP>(p, m0 + r, m0, m1) * (uint32_t)(2 * K) + 16 * piece;
+    }
+  };
   // B codes: KiB-chunks of 32 rows x 32 B; wave w takes chunks 2w, 2w+1 (the
   // weight rows 64w .. 64w+63), all rows of one matrix (gate/up: waves 0-1
   // gate rows, waves 2-3 up rows).
@@ -196,30 +212,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int wr = wr0 < N ? wr0 : N - 1;
     boff[i] = (uint32_t)wr * (K / 2) + 16 * piece;
   }
-  // scale words: wave w the weight rows 64w + lane
+  // scale chunks: wave w the weight rows 64w .. 64w+63
   constexpr int kSpr = (FMT == FMT_NVFP4) ? 16 : 32;  // K per scale byte
+  const uint32_t s_pitch = K / kSpr;                   // scale bytes per weight row
   const __amdgpu_buffer_rsrc_t rs =
-      buf_rsrc(reinterpret_cast<const uint8_t*>(wq.scales) + e * wq.stride_scales, (uint32_t)N * (K / kSpr));
-  uint32_t soff;
-  {
-    const int r = 64 * wave + lane;
-    const int wr0 = (OP == kOpGateUp) ? n0 + (r & (BN / 2 - 1)) : n0 + r;
-    const int wr = wr0 < N ? wr0 : N - 1;
-    soff = (uint32_t)wr * (K / kSpr);
-  }
-  const int sdst = D::s_off + 64 * D::s_pitch * wave;
+      buf_rsrc(reinterpret_cast<const uint8_t*>(wq.scales) + e * wq.stride_scales, (uint32_t)N * s_pitch);
 
   // the stage is a compile-time constant so that every LDS address of a step
   // is a per-lane base plus an immediate offset
-  auto issue = [&](int ks, auto stage_t) {
+  auto issue = [&](int ks, auto stage_t, auto rv_t) {
+    constexpr int NA = decltype(rv_t)::value / 2;
     uint8_t* st = lds + decltype(stage_t)::value * D::stage;
 #pragma unroll
-    for (int i = 0; i < kAPerWave; ++i)
-      dma_buf<16>(ra, aoff[i], ks * BK * 2, st + D::a_off + 1024 * (kAPerWave * wave + i));
+    for (int i = 0; i < NA; ++i)
+      dma_buf<16>(ra, aoff[i], ks * BK * 2, st + D::a_off + 1024 * (NA * wave + i));
 #pragma unroll
     for (int i = 0; i < kBPerWave; ++i)
       dma_buf<16>(rb, boff[i], ks * (BK / 2), st + D::b_off + 1024 * (kBPerWave * wave + i));
-    dma_buf<D::s_row>(rs, soff, ks * D::s_row, st + sdst);
+  };
+  // scale chunk q (steps kSC q .. kSC q + kSC - 1) into buffer q % 2: row
+  // [r][16 B] with r the tile row.  The chunk's byte offset is part of the
+  // lane offset, so bytes past the last row's end read zeros (never used).
+  auto issue_scales = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < D::kSpi; ++i) {
+      const int r = 64 * wave + D::kRpi * i + lane / D::kLpr;
+      const int wr0 = (OP == kOpGateUp) ? n0 + (r & (BN / 2 - 1)) : n0 + r;
+      const int wr = wr0 < N ? wr0 : N - 1;
+      const uint32_t off = (uint32_t)wr * s_pitch + (D::kSC * q + lane % D::kLpr) * D::s_row;
+      dma_buf<D::s_row>(rs, off, 0, lds + D::s_off + (q & 1) * D::s_buf + 16 * (64 * wave + D::kRpi * i));
+    }
+  };
+  // the scale bytes of step j (buffer, step within the chunk), uniform
+  auto sbase = [&](int j) {
+    return lds + D::s_off + ((j / D::kSC) & 1) * D::s_buf + (j % D::kSC) * 4;
   };
 
   // Wavefront grid KWM x KWN over the 128 x 256 tile; each wavefront holds R x
@@ -265,7 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int h = 0; h < 2; ++h) {
     a_lane[h] = D::a_off + (kWaveRows * wm + lr) * 128 + 16 * ((4 * h + g) ^ ((lr >> 1) & 7));
     b_lane[h] = D::b_off + (wcol + lr) * 32 + 16 * (h ^ ((lr >> 3) & 1)) + 4 * g;
-    s_lane[h] = D::s_off + (wcol + lr) * D::s_pitch + ((FMT == FMT_NVFP4) ? 2 * h + (g >> 1) : h);
+    s_lane[h] = (wcol + lr) * 16 + ((FMT == FMT_NVFP4) ? 2 * h + (g >> 1) : h);
   }
 
   // Software pipeline over half-steps.  While the MFMAs of one half run, the
@@ -275,11 +301,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // half's B fragments.  Only the first half of a tile waits for its decode.
   bf16x8 acur[R], bcur[C], bnxt[C];
   uint32_t rd[C], rsb[C];  // raw code words and scale bytes of the next half
-  auto read_raw = [&](const uint8_t* st, int h) {
+  auto read_raw = [&](const uint8_t* st, const uint8_t* sp, int h) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       rd[c] = *reinterpret_cast<const uint32_t*>(st + b_lane[h] + ccol(c) * 32);
-      rsb[c] = st[s_lane[h] + ccol(c) * D::s_pitch];
+      rsb[c] = sp[s_lane[h] + ccol(c) * 16];
     }
   };
   auto read_a = [&](const uint8_t* st, int h, int r) {
@@ -288,13 +314,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // decode VALU ops per B fragment (NVFP4: E4M3 scale, 4 conversions, 8
   // multiplies, 4 packs; MXFP4: 4 scaled conversions and the scale shift)
   constexpr int kDecV = (FMT == FMT_NVFP4) ? 17 : 5;
-  // One half: MFMAs on (acur, bcur); reads of stage `stn`, half hn; bnxt
+  // One half: MFMAs on (acur, bcur); reads of stage `stn` (scales at `spn`),
+  // half hn; bnxt
   // decoded.  Instruction order: fragment row 0's MFMAs take the 2C raw reads,
   // every later MFMA but a row's last takes a share of the decode, and each
   // row's A read follows the row's last MFMA.
-  auto half = [&](const uint8_t* stn, int hn, auto rv_t) {
+  auto half = [&](const uint8_t* stn, const uint8_t* spn, int hn, auto rv_t) {
     constexpr int RV = decltype(rv_t)::value;
-    read_raw(stn, hn);
+    read_raw(stn, spn, hn);
 #pragma unroll
     for (int r = 0; r < RV; ++r) {
 #pragma unroll
@@ -331,33 +358,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int c = 0; c < C; ++c) bcur[c] = bnxt[c];
   };
 
-  // Stages: steps 0, 1 and 2 are issued up front.  Step ks: its half 0 reads
-  // the last of stage ks (half 1) into registers; then this wave's loads of
-  // step ks+1 landed (those of ks+2 may be in flight, in-order vmcnt) and all
-  // its LDS reads are done, barrier, step ks+3 is issued into the buffer of
-  // step ks, and half 1 reads half 0 of step ks+1 (at the last step: stale
-  // LDS bytes, never used).
+  // Stages: scale chunks 0 and 1 and steps 0, 1 and 2 are issued up front.
+  // Step ks: its half 0 reads the last of stage ks (half 1) into registers;
+  // then this wave's loads of step ks+1 landed (in-order vmcnt: what was
+  // issued after them may be in flight) and all its LDS reads are done,
+  // barrier; if step ks was the last of a scale chunk, the chunk after next
+  // is issued into its buffer; step ks+3 is issued into the buffer of step
+  // ks; half 1 reads half 0 of step ks+1 (at the last step: stale LDS bytes,
+  // never used).  A scale chunk is issued kSC >= 4 steps before its first use,
+  // so it has landed whenever the step issued after it has.
   static_assert(kStages == 3, "the step loop below is unrolled by three");
+  static_assert(D::kSC >= 4, "scale chunks are issued at least 4 steps ahead");
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
+  // a scale chunk issued at the middle of step j
+  auto scales_at = [&](int j) { return j >= 0 && (j + 1) % D::kSC == 0 && (j + 1 + D::kSC) < nk; };
   auto step = [&](int ks, auto stage_t, auto rv_t) {
     constexpr int SC = decltype(stage_t)::value;
-    half(lds + SC * D::stage, 1, rv_t);
-    if (ks + 2 < nk)
-      wait_vm_lds<kDmaPerStage>();
-    else
-      wait_vm_lds<0>();
+    constexpr int kDmaPerStage = dma_per_stage<decltype(rv_t)::value>();
+    half(lds + SC * D::stage, sbase(ks), 1, rv_t);
+    // issued after step ks+1 (at the middle of step ks-1): a scale chunk, then step ks+2
+    const bool s_prev = scales_at(ks - 1);
+    if (ks + 2 < nk) {
+      if (s_prev)
+        wait_vm_lds<kDmaPerStage + D::kSpi>();
+      else
+        wait_vm_lds<kDmaPerStage>();
+    } else {
+      if (s_prev)
+        wait_vm_lds<D::kSpi>();
+      else
+        wait_vm_lds<0>();
+    }
     __builtin_amdgcn_s_barrier();
-    if (ks + 3 < nk) issue(ks + 3, stage_t);
-    half(lds + ((SC + 1) % kStages) * D::stage, 0, rv_t);
+    if (scales_at(ks)) issue_scales((ks + 1) / D::kSC + 1);
+    if (ks + 3 < nk) issue(ks + 3, stage_t, rv_t);
+    half(lds + ((SC + 1) % kStages) * D::stage, sbase(ks + 1), 0, rv_t);
   };
   // RV: the 16-row fragment rows multiplied (a partial tile skips the rest)
   auto main_loop = [&](auto rv_t) {
     constexpr int RV = decltype(rv_t)::value;
-    issue(0, S0{});
-    if (nk > 1) issue(1, S1{});
-    if (nk > 2) issue(2, S2{});
+    constexpr int kDmaPerStage = dma_per_stage<RV>();
+    set_aoff(rv_t);
+    issue_scales(0);
+    if (D::kSC < nk) issue_scales(1);
+    issue(0, S0{}, rv_t);
+    if (nk > 1) issue(1, S1{}, rv_t);
+    if (nk > 2) issue(2, S2{}, rv_t);
     if (nk > 2)
       wait_vm_lds<2 * kDmaPerStage>();
     else if (nk > 1)
@@ -365,7 +413,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     else
       wait_vm_lds<0>();
     __builtin_amdgcn_s_barrier();
-    read_raw(lds, 0);
+    read_raw(lds, sbase(0), 0);
 #pragma unroll
     for (int r = 0; r < RV; ++r) acur[r] = read_a(lds, 0, r);
 #pragma unroll
