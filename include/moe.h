@@ -114,11 +114,15 @@ const char* moe_last_error(void);
 /* Host-only check of a layer descriptor (no HIP call): MOE_OK or a negative code. */
 int32_t moe_validate_layer(const moe_layer_desc* L);
 
-/* Workspace bytes every entry point below needs for this layer and T tokens.
- * A workspace of at least this size (256-byte aligned device memory) serves
- * any call with the same (L, T) or smaller T; it needs no initialisation.
- * Calls that share a workspace must not overlap in time.  Returns 0 when the
- * descriptor is invalid. */
+/* Workspace bytes every entry point below needs for this layer and T tokens:
+ * the memory a call uses is planned and sized before anything is allocated
+ * or launched (gitee "dgpp" README, "Highlights": the startup memory plan is
+ * checked before allocation; "Request capacity and memory").  A workspace of
+ * at least this size (256-byte aligned device memory) serves any call with
+ * the same (L, T) or smaller T; it needs no initialisation (no kernel reads a
+ * workspace byte the same call has not written).  Calls that share a
+ * workspace must not overlap in time.  Returns 0 when the descriptor is
+ * invalid or T < 0; T == 0 gives one 256-byte unit. */
 size_t moe_workspace_size(const moe_layer_desc* L, int32_t T);
 
 /* Router softmax + top-k (the router function, top-k and tie rule are not on
@@ -137,8 +141,11 @@ int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits
                        int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                        void* stream);
 
-/* Grouping of the T*k (token, slot) pairs by expert: a stable counting sort
- * (pairs in t-major, slot order within each expert).
+/* Grouping of the T*k (token, slot) pairs by expert, the step that lets the
+ * expert GEMMs run over a compact list of the routed segments instead of a
+ * grid over the longest one (gitee "dgpp" README, "Configuration", "Execution
+ * and performance": engine.expert_tile_list): a stable counting sort (pairs
+ * in t-major, slot order within each expert).
  *   topk_ids int32 [T][k] with values in [0, E) (out-of-range ids are dropped).
  *   counts [E]; offsets [E+1] (exclusive scan of counts);
  *   perm_to_pair [T*k]: permuted row -> pair t*k+j (the first offsets[E]
@@ -186,11 +193,22 @@ int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pai
                     const float* y_shared, int32_t T, int32_t k, int32_t H, uint16_t* out,
                     void* stream);
 
-/* The whole layer: route, group, gate/up + SwiGLU, down, shared expert,
- * combine.  x bf16 [T][H] -> out bf16 [T][H].  Optional debug outputs
- * (NULL to skip): logits fp32 [T][E], ids int32 [T][k], weights fp32 [T][k].
- * T <= 8 runs the decode lowering (weights streamed once per active expert);
- * larger T the prefill lowering (grouped GEMM over a tile list). */
+/* The whole layer on checkpoint-format expert weights with no dequantized
+ * copy (the "DGPP" README intro: checkpoints served as published; forum
+ * thread "DGPP: a GB10-optimized C++/CUDA inference engine", opening post:
+ * NVFP4 / MXFP4 routed experts, FP8 block-128 experts and shared experts,
+ * activations BF16): route, group, gate/up + SwiGLU, down, shared expert,
+ * combine.  x bf16 [T][H] -> out bf16 [T][H], both 16-byte aligned device
+ * memory owned by the caller.  Optional debug outputs (NULL to skip): logits
+ * fp32 [T][E], ids int32 [T][k], weights fp32 [T][k].  The lowering follows
+ * the row count (gitee "dgpp" README, "Highlights": row-aware execution):
+ * T <= 8 runs the decode lowering (each active expert's weights streamed once
+ * for all its tokens), 9..64 the expert GEMV, larger T the grouped GEMM over
+ * a tile list.  Errors: MOE_ERR_INVALID_ARG (T < 0, null or misaligned x /
+ * out), MOE_ERR_WORKSPACE (ws null, misaligned or below
+ * moe_workspace_size(L, T)), MOE_ERR_UNSUPPORTED (a shape or format the
+ * descriptor check rejects), MOE_ERR_HIP (a launch failed; moe_last_error
+ * gives the text).  T == 0 returns MOE_OK and launches nothing. */
 int32_t moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16_t* out,
                           void* ws, size_t ws_bytes, float* dbg_logits, int32_t* dbg_ids,
                           float* dbg_w, void* stream);
