@@ -122,7 +122,10 @@ int32_t moe_validate_layer(const moe_layer_desc* L);
  * the same (L, T) or smaller T; it needs no initialisation (no kernel reads a
  * workspace byte the same call has not written).  Calls that share a
  * workspace must not overlap in time.  Returns 0 when the descriptor is
- * invalid or T < 0; T == 0 gives one 256-byte unit. */
+ * invalid, T < 0, or T is beyond the row limit every entry point shares (at
+ * most 2^24 (token, slot) pairs, T times each of H, I, I_shared and E below
+ * 2^31; above it the entry points return MOE_ERR_UNSUPPORTED); T == 0 gives
+ * one 256-byte unit. */
 size_t moe_workspace_size(const moe_layer_desc* L, int32_t T);
 
 /* Router softmax + top-k (the router function, top-k and tie rule are not on
@@ -152,6 +155,8 @@ int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits
  *            entries); pair_to_perm [T*k]: inverse, -1 for a dropped pair.
  *   active_experts int32 [E+1] or NULL: element 0 = number of experts with at
  *            least one row, then their ids in increasing order.
+ * At most 2^24 pairs (T*k); more returns MOE_ERR_UNSUPPORTED (and a
+ * workspace size of 0).
  * Workspace: moe_permute_workspace_size(T, k, E) bytes. */
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
 int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,

@@ -65,6 +65,34 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(driver: str, out_dir: str, jobs: int | None = None) -> str:
+    """Every library source plus a host test driver, with AddressSanitizer and
+    UndefinedBehaviorSanitizer on the host code only (the device code is
+    built as usual; the driver exercises validation, workspace planning and
+    argument checks, and never launches).  Returns the executable's path."""
+    os.makedirs(out_dir, exist_ok=True)
+    cc = hipcc()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = [f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument", *san]
+
+    def compile_one(src):
+        obj = os.path.join(out_dir, os.path.basename(src).rsplit(".", 1)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        _run([cc, *flags, *lang, "-c", src, "-o", obj])
+        return obj
+
+    srcs = [os.path.join(CSRC, s) for s in SOURCES] + [driver]
+    n = jobs or min(len(srcs), os.cpu_count() or 1, 8)
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    exe = os.path.join(out_dir, "host_checks")
+    _run([cc, f"--offload-arch={ARCH}", *san, "-o", exe, *objs])
+    return exe
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)

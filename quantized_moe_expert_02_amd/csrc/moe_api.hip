@@ -6,6 +6,7 @@
 // Here that means: every descriptor and size is checked on the host, a
 // negative status comes back before any launch, and the caller sizes the
 // workspace from moe_workspace_size() up front.
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -166,6 +167,18 @@ constexpr int kGemvMaxRows = 64;
 // The matrix-core router's error bound assumes H * 2^-23 << 1.
 constexpr int kMfmaRouterMaxH = 1 << 16;
 
+// Row counts the kernels index with 32-bit integers: at most 2^24 (token,
+// slot) pairs, and every token-major buffer (T rows of H, I, I_shared or E
+// elements) below 2^31 elements.  Larger T is MOE_ERR_UNSUPPORTED.
+constexpr int64_t kMaxPairs = int64_t(1) << 24;
+
+bool rows_ok(const moe_layer_desc* L, int T) {
+  if (T < 0) return false;
+  const int64_t w = std::max({L->H, L->I, L->E, L->has_shared ? L->I_shared : 0});
+  return (int64_t)T * L->top_k <= kMaxPairs && (int64_t)T * w < (int64_t(1) << 31);
+}
+
+// Only for T with rows_ok (its int products stay in range).
 WsPlan plan(const moe_layer_desc* L, int T) {
   WsPlan p;
   const int E = L->E, k = L->top_k;
@@ -446,6 +459,7 @@ int32_t layer_impl(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16
       return MOE_ERR_UNSUPPORTED;
   }
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!rows_ok(L, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (x == nullptr || out == nullptr || !aligned(x, 16) || !aligned(out, 16))
     return MOE_ERR_INVALID_ARG;
@@ -553,7 +567,7 @@ const char* moe_status_string(int32_t status) {
 int32_t moe_validate_layer(const moe_layer_desc* L) { return check_layer(L); }
 
 size_t moe_workspace_size(const moe_layer_desc* L, int32_t T) {
-  if (check_layer(L) != MOE_OK || T < 0) return 0;
+  if (check_layer(L) != MOE_OK || !rows_ok(L, T)) return 0;
   if (T == 0) return kAlign;
   return plan(L, T).total;
 }
@@ -563,6 +577,7 @@ int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits
   int32_t st = check_layer(L);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!rows_ok(L, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARG;
   if (x != nullptr && (!aligned(x, 16) || L->H % 8 != 0)) return MOE_ERR_INVALID_ARG;
@@ -574,6 +589,7 @@ int32_t moe_route_topk(const moe_layer_desc* L, const uint16_t* x, float* logits
 
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
   if (T < 0 || k <= 0 || E <= 0 || E > kMaxExperts) return 0;
+  if ((int64_t)T * k > kMaxPairs) return 0;
   const PermPlan pp = perm_plan(T, k);
   return align_up((size_t)pp.NB * E * 4) + align_up((size_t)(E + 1) * 4);
 }
@@ -582,7 +598,7 @@ int32_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, in
                     int32_t* offsets, int32_t* perm_to_pair, int32_t* pair_to_perm,
                     int32_t* active_experts, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || k <= 0 || E <= 0 || k > E) return MOE_ERR_INVALID_ARG;
-  if (E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxExperts || (int64_t)T * k > kMaxPairs) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!topk_ids || !counts || !offsets || !perm_to_pair || !pair_to_perm) return MOE_ERR_INVALID_ARG;
   const size_t need = moe_permute_workspace_size(T, k, E);
@@ -605,6 +621,7 @@ int32_t moe_expert_gemm(int32_t op, const moe_layer_desc* L, int32_t shared,
   if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
   if (shared && !L->has_shared) return MOE_ERR_INVALID_ARG;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!rows_ok(L, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (in == nullptr || out == nullptr || !aligned(in, 16) || !aligned(out, 16))
     return MOE_ERR_INVALID_ARG;
@@ -649,6 +666,7 @@ int32_t moe_decode_gate_up(const moe_layer_desc* L, const uint16_t* x, int32_t T
   int32_t st = check_layer(L);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!rows_ok(L, T)) return MOE_ERR_UNSUPPORTED;
   if (T > kDecodeRows) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (x == nullptr || topk_ids == nullptr || h == nullptr || !aligned(x, 16) || !aligned(h, 16) ||
@@ -670,6 +688,7 @@ int32_t moe_layer_forward_noalloc(const moe_layer_desc* L, const uint16_t* x, in
   int32_t st = check_layer(L);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!rows_ok(L, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (x == nullptr || out == nullptr || !aligned(x, 16) || !aligned(out, 16))
     return MOE_ERR_INVALID_ARG;
@@ -716,6 +735,7 @@ int32_t moe_route_table(const moe_layer_desc* L, const uint16_t* x, float* logit
   int32_t st = check_layer(L);
   if (st != MOE_OK) return st;
   if (T < 0 || V <= 0) return MOE_ERR_INVALID_ARG;
+  if (!rows_ok(L, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (token_ids == nullptr || table == nullptr || topk_ids == nullptr || topk_w == nullptr)
     return MOE_ERR_INVALID_ARG;
@@ -759,6 +779,7 @@ int32_t moe_expert_gemm_q(int32_t mode, int32_t op, const moe_layer_desc* L, int
   if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
   if (shared && !L->has_shared) return MOE_ERR_INVALID_ARG;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!rows_ok(L, T)) return MOE_ERR_UNSUPPORTED;
   const moe_qweight& wq = (op == MOE_OP_GATE_UP_SWIGLU) ? (shared ? L->sh_gate : L->gate)
                                                         : (shared ? L->sh_down : L->down);
   if (!mode_applies(mode, wq.format) || wq.cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
