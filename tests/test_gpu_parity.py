@@ -201,9 +201,9 @@ EDGE_COUNTS = [0, 1, 127, 128, 129, 0, 256, 300]
 
 @pytest.mark.parametrize("fmt,H,I", [(synth.FMT_NVFP4, 352, 160), (synth.FMT_MXFP4, 416, 224),
                                      (synth.FMT_FP8, 336, 144),
-                                     # K % 64 == 0: the LDS-DMA kernel (MXFP4 2 x 2
-                                     # and NVFP4 1 x 4 wavefront grids), ragged
-                                     # column tails
+                                     # K % 64 == 0: the LDS-DMA kernel (128 x 256
+                                     # tiles, 1 x 4 wavefront grid for both FP4
+                                     # formats), ragged column tails
                                      (synth.FMT_MXFP4, 384, 224), (synth.FMT_MXFP4, 448, 320),
                                      (synth.FMT_NVFP4, 480, 192), (synth.FMT_NVFP4, 448, 224)])
 def test_grouped_gemm_tile_edges(fmt, H, I):
