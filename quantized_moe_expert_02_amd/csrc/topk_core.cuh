@@ -706,7 +706,7 @@ struct BlockFastTopkSmem {
   uint32_t wthr[NTH / kWave];
   int ncand;
   int ok;
-  int cand[kWave];  // reads in groups of 8 stay inside (nc <= 64)
+  int cand[kWave];  // each thread reads its span of these (nc <= 64)
   uint64_t ckey[kWave];
   double tv[kMaxTopK + 1];
   int ti[kMaxTopK + 1];
@@ -771,23 +771,36 @@ __device__ inline bool block_topk_fast(const double* vals, int E, int k, int ren
   __syncthreads();
   const int nc = sm.ncand;
   if (nc > kWave || renorm == 0) return false;  // uniform: every thread read the same nc
-  if ((int)threadIdx.x < nc) {
-    const int e = sm.cand[threadIdx.x];
-    const uint64_t ke = sm.ckey[threadIdx.x];
+  // Rank of each candidate among all nc: the comparisons are split over
+  // kParts consecutive threads per candidate (kSpan candidates each), and
+  // their counts summed with lane shuffles, so the block does the nc x nc
+  // comparisons in kSpan steps instead of one thread doing nc.
+  static_assert(NTH % kWave == 0 && NTH / kWave >= 1, "whole wavefronts");
+  constexpr int kParts = NTH / kWave;      // threads per candidate
+  constexpr int kSpan = kWave / kParts;     // candidates each thread compares with
+  static_assert(kParts * kSpan == kWave && (kParts & (kParts - 1)) == 0, "power-of-two split");
+  {
+    const int ci = threadIdx.x / kParts, part = threadIdx.x % kParts;
     int cnt = 0;
-    for (int j0 = 0; j0 < nc; j0 += 8) {
-      uint64_t kj[8];
-      int ej[8];
+    uint64_t ke = 0ull;
+    int e = 0;
+    if (ci < nc) {
+      e = sm.cand[ci];
+      ke = sm.ckey[ci];
+      uint64_t kj[kSpan];
+      int ej[kSpan];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        kj[q] = sm.ckey[j0 + q];
-        ej[q] = sm.cand[j0 + q];
+      for (int q = 0; q < kSpan; ++q) {
+        kj[q] = sm.ckey[part * kSpan + q];
+        ej[q] = sm.cand[part * kSpan + q];
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (j0 + q < nc) cnt += ranks_before(kj[q], ej[q], ke, e);
+      for (int q = 0; q < kSpan; ++q)
+        if (part * kSpan + q < nc) cnt += ranks_before(kj[q], ej[q], ke, e);
     }
-    if (cnt < K1) {
+#pragma unroll
+    for (int d = 1; d < kParts; d <<= 1) cnt += __shfl_xor(cnt, d, kWave);
+    if (ci < nc && part == 0 && cnt < K1) {
       sm.tv[cnt] = (ke == 1ull) ? __builtin_nan("") : vals[e];
       sm.ti[cnt] = e;
     }
