@@ -161,6 +161,7 @@ struct DecodeArgs {
   uint16_t* h;        // [T*k][I], row = pair t*k+j
   uint16_t* hs;       // [T][I_shared]
   uint16_t* out;      // [T][H]
+  int dc_stage_k;     // down-combine launch: input rows staged in LDS, per-wave row length (0: not)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Routing alone with the decode router (128-row slices, token groups of 8)
