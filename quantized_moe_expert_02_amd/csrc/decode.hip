@@ -35,7 +35,7 @@ constexpr int kRSBatch = 16;
 
 template <int NT>
 struct RouterSmem {
-  float xs[NT][kRH];
+  __attribute__((aligned(16))) float xs[kRH][NT];  // the NT tokens of one row together
   double red[8][NT][kRouterCols];
   float reda[8][NT][kRouterCols];
 };
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
   }
   for (int i = threadIdx.x; i < NT * kRH; i += 256) {
     const int t = i / kRH, h = i % kRH;
-    sm.xs[t][h] = (t < nt && h < nh) ? bf16_to_f32(a.x[(size_t)(t0 + t) * H + h0 + h]) : 0.f;
+    sm.xs[h][t] = (t < nt && h < nh) ? bf16_to_f32(a.x[(size_t)(t0 + t) * H + h0 + h]) : 0.f;
   }
   __syncthreads();
   double acc[NT];
@@ -74,17 +74,20 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
     acc[t] = 0.0;
     aa[t] = 0.f;
   }
+  // Rows of tokens past the batch are zero in LDS, so every token slot runs
+  // unguarded (their sums are never stored).
 #pragma unroll
   for (int j = 0; j < kRH / 8; ++j) {
     const int h = rg + 8 * j;
     const double wd = wv[j];
     const float wa = fabsf(wv[j]);
+    float xv[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (NT == 1 || t < nt) {  // bf16 * fp32 is exact in float64
-        acc[t] = fma(static_cast<double>(sm.xs[t][h]), wd, acc[t]);
-        aa[t] = fmaf(fabsf(sm.xs[t][h]), wa, aa[t]);
-      }
+    for (int t = 0; t < NT; ++t) xv[t] = sm.xs[h][t];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {  // bf16 * fp32 is exact in float64
+      acc[t] = fma(static_cast<double>(xv[t]), wd, acc[t]);
+      aa[t] = fmaf(fabsf(xv[t]), wa, aa[t]);
     }
   }
 #pragma unroll
