@@ -257,7 +257,22 @@ __host__ __device__ __forceinline__ bool lean_fits(const DecodeArgs& a) {
   return a.gate.wide && a.up.wide && a.H % kLeanKStep == 0 && a.H <= kLeanMaxK;
 }
 
-template <int FMT>
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One token: its input row does not depend on the routing, so each
+// wavefront copies its quarter of the row into LDS by DMA (no register round
+// trip) before the routed ids are read.
+__device__ __forceinline__ void lean_x_dma(const DecodeArgs& a, LeanSmem& sm) {
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.x), (short)0, a.H * 2, 0x00020000);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  for (int i = wave * kWave * 8; i < a.H; i += kWave * kGuWK * 8)  // 512 values per wavefront step
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(sm.x + i), 16, 2 * i + 16 * lane, 0, 0,
+                                             0);
+}
+
+// XDMA: the input row is already on its way by lean_x_dma (one token).
+template <int FMT, bool XDMA>
 __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const int* toks,
                                     const int* pairs, int tile, LeanSmem& sm) {
   static_assert(FMT == FMT_NVFP4 || FMT == FMT_MXFP4, "FP4 layouts");
@@ -265,10 +280,12 @@ __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
   // the group's input rows into LDS (16-byte pieces, every thread)
-  for (int i = threadIdx.x * 8; i < nrows * H; i += kWave * kGuWK * 8) {
-    const int row = i / H, k = i - row * H;
-    *reinterpret_cast<u32x4*>(&sm.x[i]) =
-        *reinterpret_cast<const u32x4*>(a.x + (size_t)toks[row] * H + k);
+  if constexpr (!XDMA) {
+    for (int i = threadIdx.x * 8; i < nrows * H; i += kWave * kGuWK * 8) {
+      const int row = i / H, k = i - row * H;
+      *reinterpret_cast<u32x4*>(&sm.x[i]) =
+          *reinterpret_cast<const u32x4*>(a.x + (size_t)toks[row] * H + k);
+    }
   }
   const int n0 = tile * 16;
   const int rb = H / 2;  // code bytes per row
@@ -283,6 +300,7 @@ __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const
     tsg = a.gate.tscale[e];
     tsu = a.up.tscale[e];
   }
+  if constexpr (XDMA) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();  // x staged
   f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
   const uint16_t* xr = (r < nrows) ? sm.x + r * H : nullptr;
@@ -362,12 +380,22 @@ __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs
   const int ntiles = a.I / gemv_rows_per_block<kOpGateUp>();
   const int b = blockIdx.x - nsg;
   const int q = b / ntiles, tile = b % ntiles;
+  extern __shared__ __attribute__((aligned(16))) char lean_dyn[];
+  LeanSmem& lsm = *reinterpret_cast<LeanSmem*>(lean_dyn);
+  constexpr bool kFp4 = RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4;
+  const bool lean = kFp4 && lean_fits(a);
+  if (kFp4 && lean && a.T == 1) lean_x_dma(a, lsm);
   int e, n;
-  if (!derive_group(a, q, grp, e, n)) return;
-  if constexpr (RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4) {
-    if (lean_fits(a)) {
-      extern __shared__ __attribute__((aligned(16))) char lean_dyn[];
-      gate_up_lean<RFMT>(a, e, n, grp.toks, grp.pairs, tile, *reinterpret_cast<LeanSmem*>(lean_dyn));
+  if (!derive_group(a, q, grp, e, n)) {
+    if (kFp4 && lean && a.T == 1) __builtin_amdgcn_s_waitcnt(0x0f70);  // no DMA outlives its block
+    return;
+  }
+  if constexpr (kFp4) {
+    if (lean) {
+      if (a.T == 1)
+        gate_up_lean<RFMT, true>(a, e, n, grp.toks, grp.pairs, tile, lsm);
+      else
+        gate_up_lean<RFMT, false>(a, e, n, grp.toks, grp.pairs, tile, lsm);
       return;
     }
   }
