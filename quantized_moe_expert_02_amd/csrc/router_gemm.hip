@@ -36,7 +36,7 @@ constexpr int RBM = 128, RBN = 64, RBK = 64;
 // K pieces in the order piece (h, i) of K half h -> column 8(2i + h), for A
 // and B alike, so an MFMA still pairs equal K.
 constexpr int RLDS = RBK + 16;
-constexpr int kSplitRows = 128;  // router rows per block of the split pass
+constexpr int kSplitRows = 32;  // router rows per block of the split pass (8 per wavefront)
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
@@ -56,8 +56,8 @@ __device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uin
 
 // Wr [H][E] fp32 -> planes [3][E][H] bf16, a transposed fp32 copy wrt [E][H]
 // (for the exact recompute of contested logits, read along h), and wsq
-// [HB][E] float64 sums of w^2 over router rows [hb*128, +128).
-// Block: 64 experts x 128 rows; lane = expert.
+// [HB][E] float64 sums of w^2 over router rows [hb*32, +32).
+// Block: 64 experts x 32 rows; lane = expert (512 blocks at H = 2048, E = 512).
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, int H,
                                                            int E, uint16_t* __restrict__ planes,
                                                            float* __restrict__ wrt,
@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + lane;
   const int hb = blockIdx.y;
-  const int h0 = hb * kSplitRows + wave * 32;
+  const int h0 = hb * kSplitRows + wave * (kSplitRows / 4);
   double sq = 0.0;
   if (e < E) {
-    for (int c = 0; c < 32; c += 8) {
+    for (int c = 0; c < kSplitRows / 4; c += 8) {
       const int h = h0 + c;
       if (h >= H) break;  // H % 8 == 0: a group of 8 rows is all in or all out
       uint32_t p[3][4];
@@ -115,15 +115,23 @@ struct RouterMfmaArgs {
   int n_mt, n_nt;
 };
 
-// One LDS stage (50 KB): two workgroups fit on a CU, so a 512-tile grid runs
-// in one round; the next step waits in registers while this one is read.
+// One LDS stage (50 KB); the next step waits in registers while this one is
+// read.  Eight wavefronts of 32 tokens x 32 experts (float64 step sums in 32
+// registers a lane) let two workgroups share a CU, so a 512-tile grid runs in
+// one round: 80 -> 74 us on 8192 tokens x 512 experts against four
+// wavefronts of 64 x 32.
+// (16-byte aligned rows: every fragment access is one 128-bit LDS
+// instruction; with the element type's 2-byte alignment the compiler splits
+// each into two pairs of 32-bit accesses)
 struct RouterSmem {
-  uint16_t a[RBM][RLDS];
-  uint16_t b[3][RBN][RLDS];
+  __attribute__((aligned(16))) uint16_t a[RBM][RLDS];
+  __attribute__((aligned(16))) uint16_t b[3][RBN][RLDS];
   float wn[RBN];
 };
 
-__global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
+constexpr int kRThreads = 512;
+
+__global__ __launch_bounds__(kRThreads, 4) void router_mfma_kernel(RouterMfmaArgs a) {
   __shared__ RouterSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-aware order (workgroup b runs on XCD b % 8): each XCD takes a
@@ -142,28 +150,34 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
     float wn = 0.f;
     if (e < E) {
       double s = 0.0;
-      for (int hb = 0; hb < a.HB; ++hb) s += a.wsq[(size_t)hb * E + e];
+      for (int hb0 = 0; hb0 < a.HB; hb0 += 8) {  // eight loads in flight at a time
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (hb0 + j < a.HB) ? a.wsq[(size_t)(hb0 + j) * E + e] : 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += v[j];
+      }
       wn = static_cast<float>(sqrt(s) * (1.0 + 0x1p-40)) * (1.0f + 0x1p-21f);
     }
     sm.wn[tid] = wn;
   }
 
-  // staging roles
-  const int srow = tid >> 1, shalf = tid & 1;
+  // staging roles: four threads per token row, two 8-element K pieces each
+  const int srow = tid >> 2, squart = tid & 3;
   const uint16_t* xrow = (t0 + srow < a.T) ? a.x + (size_t)(t0 + srow) * H : nullptr;
   float xsq = 0.f;
 
-  u32x4 ra[4], rb[6];
+  u32x4 ra[2], rb[3];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + 32 * shalf + 8 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int k = k0 + 8 * (2 * squart + i);
       ra[i] = (xrow != nullptr && k < H) ? *reinterpret_cast<const u32x4*>(xrow + k)
                                          : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int c = tid + 256 * i;       // 192 rows x 8 chunks of 8
+    for (int i = 0; i < 3; ++i) {
+      const int c = tid + kRThreads * i;  // 192 rows x 8 chunks of 8
       const int row = c >> 3, part = c & 7;
       const int s = row / RBN, e = e0 + row % RBN;
       const int k = k0 + 8 * part;
@@ -174,8 +188,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
   };
   auto store = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sm.a[srow][8 * (2 * i + shalf)]) = ra[i];
+    for (int i = 0; i < 2; ++i) {
+      const int pc = 2 * squart + i;  // K piece (half pc / 4, index pc % 4)
+      *reinterpret_cast<u32x4*>(&sm.a[srow][8 * (2 * (pc & 3) + (pc >> 2))]) = ra[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float lo = __uint_as_float(ra[i][j] << 16), hi = __uint_as_float(ra[i][j] & 0xffff0000u);
@@ -184,18 +199,18 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < 3; ++i) {
+      const int c = tid + kRThreads * i;
       const int row = c >> 3, part = c & 7;  // K piece (half part / 4, index part % 4)
       *reinterpret_cast<u32x4*>(&sm.b[row / RBN][row % RBN][8 * (2 * (part & 3) + (part >> 2))]) = rb[i];
     }
   };
 
-  // MFMA roles: wave (wm, wn) owns tokens [64wm, +64) x experts [32wn, +32)
+  // MFMA roles: wave (wm, wn) owns tokens [32wm, +32) x experts [32wn, +32)
   const int wm = wave >> 1, wn = wave & 1;
-  double dacc[4][2][4];
+  double dacc[2][2][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -208,18 +223,18 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
   for (int ks = 0; ks < nk; ++ks) {
     const bool more = ks + 1 < nk;
     if (more) load((ks + 1) * RBK);
-    f32x4 cacc[4][2];
+    f32x4 cacc[2][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int c = 0; c < 2; ++c) cacc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < RBK; kk += 32) {
       const int ko = kk + 8 * (lane >> 4);
-      bf16x8 af[4];
+      bf16x8 af[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        af[r] = *reinterpret_cast<const bf16x8*>(&sm.a[64 * wm + 16 * r + (lane & 15)][ko]);
+      for (int r = 0; r < 2; ++r)
+        af[r] = *reinterpret_cast<const bf16x8*>(&sm.a[32 * wm + 16 * r + (lane & 15)][ko]);
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
         bf16x8 bfr[2];
@@ -227,14 +242,14 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
         for (int c = 0; c < 2; ++c)
           bfr[c] = *reinterpret_cast<const bf16x8*>(&sm.b[s][32 * wn + 16 * c + (lane & 15)][ko]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
           for (int c = 0; c < 2; ++c)
             cacc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[c], cacc[r][c], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -246,10 +261,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
 
   // logits: lane holds tokens 4*(lane/16)+j of each 16-row tile, expert lane%16
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = t0 + 64 * wm + 16 * r + 4 * (lane >> 4) + j;
+      const int t = t0 + 32 * wm + 16 * r + 4 * (lane >> 4) + j;
       if (t >= a.T) continue;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -259,10 +274,11 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterMfmaArgs a) {
     }
 
   // per-token bound factor for this expert block
-  xsq += __shfl_xor(xsq, 1, kWave);
+  xsq += __shfl_xor(xsq, 1, kWave);  // the four threads of a token row
+  xsq += __shfl_xor(xsq, 2, kWave);
   float wmax = 0.f;
   for (int i = 0; i < RBN; ++i) wmax = fmaxf(wmax, sm.wn[i]);
-  if (shalf == 0 && t0 + srow < a.T) {
+  if (squart == 0 && t0 + srow < a.T) {
     const float xn = sqrtf(xsq) * a.xslack;
     float f = (xn + 0x1p-40f) * (wmax + 0x1p-40f) * (1.0f + 0x1p-21f);
     if (!(f < 0x1p126f)) f = __builtin_inff();  // also NaN -> inf
@@ -310,7 +326,7 @@ hipError_t launch_router_mfma(const uint16_t* x, const float* wr, int T, int H, 
   a.n_nt = router_mfma_cols(E);
   const int total = a.n_mt * a.n_nt;
   const int per = (total + kXcds - 1) / kXcds;
-  return launch(router_mfma_kernel, dim3(per * kXcds), dim3(256), 0, s, a);
+  return launch(router_mfma_kernel, dim3(per * kXcds), dim3(kRThreads), 0, s, a);
 }
 
 }  // namespace moe
