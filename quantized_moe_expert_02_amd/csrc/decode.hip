@@ -487,8 +487,9 @@ constexpr int kDcMaxWaves = 12;  // one wavefront per slot up to 12 slots (168 V
 // are staged in LDS by the whole wavefront (one 16-byte load per lane per 512
 // values) instead of being loaded by the four lanes that feed the MFMA's B
 // column (16 load instructions of 4 lanes each per 512 values, which queue in
-// the CU's address path): c1 24.9 -> 24.2 us per layer.  On larger grids the
-// staging's LDS costs more occupancy than it saves (c2 +3.6, c3 +55 us).
+// the CU's address path): one-token NVFP4 layer 24.9 -> 24.2 us.  On larger
+// grids the staging's LDS costs more occupancy than it saves (8-token NVFP4
+// layer +3.6 us, 8-token wide-FP8 layer +55 us).
 constexpr int kDcStageK = 2048;
 constexpr int kDcStageMaxBlocks = 255;
 
