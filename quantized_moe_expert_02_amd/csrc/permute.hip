@@ -37,14 +37,16 @@ __device__ int block_exclusive_scan(int v, int* tmp, int& total) {
   }
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-      const int s = tmp[w];
-      tmp[w] = run;
-      run += s;
+  if (wave == 0) {  // exclusive scan of the (at most 16) wavefront totals by lane shuffles
+    const int nw = (int)(blockDim.x >> 6);
+    const int s = (lane < nw) ? tmp[lane] : 0;
+    int y = s;
+    for (int d = 1; d < 16; d <<= 1) {
+      const int z = __shfl_up(y, d, 64);
+      if (lane >= d) y += z;
     }
-    tmp[16] = run;
+    if (lane < nw) tmp[lane] = y - s;
+    if (lane == nw - 1) tmp[16] = y;
   }
   __syncthreads();
   const int r = tmp[wave] + x - v;
@@ -68,9 +70,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(int NB, int E, int* __restri
     if (e < E) c = offsets[e + 1] - offsets[e];
   } else if (e < E) {
     // hist[b][e] becomes the rank of chunk b's first pair within expert e.
-    // The loads of a batch are issued before its stores (the stores may alias
-    // them), so a batch costs one memory round trip, not one per chunk.
-    constexpr int kB = 16;
+    // The loads of a batch (one per chunk, coalesced across the experts of a
+    // wavefront) are issued before its stores, which may alias them, so a
+    // batch costs one memory round trip: the 80 chunks of 8192 x 10 pairs
+    // take one.
+    constexpr int kB = 96;
     for (int b0 = 0; b0 < NB; b0 += kB) {
       int h[kB];
 #pragma unroll
@@ -107,26 +111,52 @@ __global__ __launch_bounds__(1024) void scan_kernel(int NB, int E, int* __restri
   }
 }
 
-// One wave per chunk; the chunk's pairs are ranked 64 at a time in order.
-__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids, int P, int E,
-                                                     const int* __restrict__ rank0,
-                                                     const int* __restrict__ offsets,
-                                                     int* __restrict__ perm_to_pair,
-                                                     int* __restrict__ pair_to_perm) {
-  __shared__ int cnt[kMaxExperts];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  // position of this chunk's first pair of expert e in the permuted order
-  for (int e = lane; e < E; e += 64) cnt[e] = offsets[e] + rank0[(size_t)b * E + e];
+// One workgroup per chunk, four wavefronts of 256 consecutive pairs each:
+// the wavefronts count their segments' experts, each expert's count is turned
+// into the segment's first position (chunk base, then the earlier segments
+// in order), and every wavefront ranks its pairs 64 at a time in order.
+constexpr int kScatterWaves = 4;
+constexpr int kScatterSeg = kPermChunk / kScatterWaves;
+
+__global__ __launch_bounds__(kWave * kScatterWaves) void scatter_kernel(
+    const int* __restrict__ ids, int P, int E, const int* __restrict__ rank0,
+    const int* __restrict__ offsets, int* __restrict__ perm_to_pair, int* __restrict__ pair_to_perm) {
+  __shared__ int cnt[kScatterWaves][kMaxExperts];
+  const int b = blockIdx.x, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < kScatterWaves * kMaxExperts; i += kWave * kScatterWaves)
+    (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int p0 = b * kPermChunk + wave * kScatterSeg, p1 = min(P, p0 + kScatterSeg);
+  constexpr int kIt = kScatterSeg / kWave;
+  int my[kIt];
+#pragma unroll
+  for (int i = 0; i < kIt; ++i) {
+    const int p = p0 + kWave * i + lane;
+    const int e = (p < p1) ? ids[p] : -1;
+    my[i] = ((unsigned)e < (unsigned)E) ? e : -1;
+    if (my[i] >= 0) atomicAdd(&cnt[wave][my[i]], 1);
+  }
+  __syncthreads();
+  // first position of each segment's pairs of expert e
+  for (int e = threadIdx.x; e < E; e += kWave * kScatterWaves) {
+    int pos = offsets[e] + rank0[(size_t)b * E + e];
+#pragma unroll
+    for (int w = 0; w < kScatterWaves; ++w) {
+      const int n = cnt[w][e];
+      cnt[w][e] = pos;
+      pos += n;
+    }
+  }
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  const int p0 = b * kPermChunk, p1 = min(P, p0 + kPermChunk);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int s = p0; s < p1; s += 64) {
-    const int p = s + lane;
-    const int e0 = (p < p1) ? ids[p] : -1;
-    const bool valid = (p < p1) && (unsigned)e0 < (unsigned)E;
-    const int e = valid ? e0 : -1;
+  int* const c = cnt[wave];
+#pragma unroll
+  for (int i = 0; i < kIt; ++i) {
+    const int p = p0 + kWave * i + lane;
+    const int e = my[i];
+    const bool valid = e >= 0;
     // lanes holding the same expert id
     uint64_t same = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -134,18 +164,18 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids
       same &= ((e >> bit) & 1) ? m : ~m;
     }
     const int rank = __popcll(same & lt);
-    int pos = 0;
-    if (valid) pos = cnt[e] + rank;
-    __syncthreads();
+    const int pos = valid ? c[e] + rank : 0;
+    __builtin_amdgcn_wave_barrier();  // every lane has read its counter
     if (valid) {
       perm_to_pair[pos] = p;
       pair_to_perm[p] = pos;
       // the last lane of each group advances the counter
-      if ((same >> lane) == 1ull) cnt[e] = pos + 1;
+      if ((same >> lane) == 1ull) c[e] = pos + 1;
     } else if (p < p1) {
       pair_to_perm[p] = -1;  // a dropped pair (expert id out of range)
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the counters, before the next reads
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -160,8 +190,8 @@ hipError_t launch_permute(const int* ids, int T, int k, int E, int* counts, int*
   e = launch(scan_kernel, dim3(1), dim3(1024), 0, s, pp.NB, E, hist, counts, offsets, act, n_act,
              tile_m, reinterpret_cast<int2*>(tiles), n_tiles, max_tiles, 0);
   if (e != hipSuccess) return e;
-  return launch(scatter_kernel, dim3(pp.NB), dim3(64), 0, s, ids, pp.P, E, hist, offsets,
-                perm_to_pair, pair_to_perm);
+  return launch(scatter_kernel, dim3(pp.NB), dim3(kWave * kScatterWaves), 0, s, ids, pp.P, E, hist,
+                offsets, perm_to_pair, pair_to_perm);
 }
 
 hipError_t launch_groups_from_offsets(const int* offsets, int E, int* act, int* n_act, int tile_m,
