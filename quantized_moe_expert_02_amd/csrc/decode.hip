@@ -272,75 +272,108 @@ __device__ __forceinline__ void lean_x_dma(const DecodeArgs& a, LeanSmem& sm) {
 }
 
 // XDMA: the input row is already on its way by lean_x_dma (one token).
-template <int FMT, bool XDMA>
+// SHARED: the shared expert (weights sg / su, expert 0, input rows = all T
+// tokens, output row t of hs); else routed expert e's group (rows toks[],
+// output rows pairs[] of h).  FP8 (block-128) chunks carry 32 codes per lane
+// in two loads and a block scale applied to each chunk's partial sum.
+template <int FMT, bool XDMA, bool SHARED>
 __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const int* toks,
                                     const int* pairs, int tile, LeanSmem& sm) {
-  static_assert(FMT == FMT_NVFP4 || FMT == FMT_MXFP4, "FP4 layouts");
-  const int H = a.H, I = a.I;
+  static_assert(FMT == FMT_NVFP4 || FMT == FMT_MXFP4 || FMT == FMT_FP8, "lean layouts");
+  constexpr bool kFp8 = FMT == FMT_FP8;
+  const WDesc& gw = SHARED ? a.sg : a.gate;
+  const WDesc& uw = SHARED ? a.su : a.up;
+  const int H = a.H, I = SHARED ? a.I_shared : a.I;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
   // the group's input rows into LDS (16-byte pieces, every thread)
   if constexpr (!XDMA) {
     for (int i = threadIdx.x * 8; i < nrows * H; i += kWave * kGuWK * 8) {
       const int row = i / H, k = i - row * H;
+      const int tok = SHARED ? row : toks[row];
       *reinterpret_cast<u32x4*>(&sm.x[i]) =
-          *reinterpret_cast<const u32x4*>(a.x + (size_t)toks[row] * H + k);
+          *reinterpret_cast<const u32x4*>(a.x + (size_t)tok * H + k);
     }
   }
   const int n0 = tile * 16;
-  const int rb = H / 2;  // code bytes per row
+  const int rb = kFp8 ? H : H / 2;  // code bytes per row
+  constexpr int cbytes = kFp8 ? 128 : 64;  // code bytes per 128-K chunk and row
+  constexpr int lbytes = kFp8 ? 32 : 16;   // of which lane group g loads
   const int spw = H / (128 * kGuWK);  // chunks per wavefront
   const int c0 = wave * spw;
-  const uint8_t* gq = a.gate.codes + e * a.gate.stride_codes + (size_t)(n0 + r) * rb + 16 * g;
-  const uint8_t* uq = a.up.codes + e * a.up.stride_codes + (size_t)(n0 + r) * rb + 16 * g;
-  const uint8_t* gs = scale_row_ptr<FMT>(a.gate, e, n0 + r);
-  const uint8_t* us = scale_row_ptr<FMT>(a.up, e, n0 + r);
+  const uint8_t* gq = gw.codes + e * gw.stride_codes + (size_t)(n0 + r) * rb + lbytes * g;
+  const uint8_t* uq = uw.codes + e * uw.stride_codes + (size_t)(n0 + r) * rb + lbytes * g;
+  const uint8_t* gs = scale_row_ptr<FMT>(gw, e, n0 + r);
+  const uint8_t* us = scale_row_ptr<FMT>(uw, e, n0 + r);
   float tsg = 1.0f, tsu = 1.0f;
   if constexpr (FMT == FMT_NVFP4) {
-    tsg = a.gate.tscale[e];
-    tsu = a.up.tscale[e];
+    tsg = gw.tscale[e];
+    tsu = uw.tscale[e];
   }
   if constexpr (XDMA) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();  // x staged
   f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
   const uint16_t* xr = (r < nrows) ? sm.x + r * H : nullptr;
-  for (int cb = c0; cb < c0 + spw; cb += 4) {
-    ARaw<FMT> pg[4], pu[4];
+  // chunks per batch of loads (FP8: two, which keeps the kernel at 104 VGPRs
+  // where four would need 152)
+  constexpr int kB = kFp8 ? 2 : 4;
+  for (int cb = c0; cb < c0 + spw; cb += kB) {
+    ARaw<FMT> pg[kB], pu[kB];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      pg[d].q = *reinterpret_cast<const u32x4*>(gq + 64 * (cb + d));
-      pu[d].q = *reinterpret_cast<const u32x4*>(uq + 64 * (cb + d));
+    for (int d = 0; d < kB; ++d) {
+      if constexpr (kFp8) {
+        pg[d].q0 = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d));
+        pg[d].q1 = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d) + 16);
+        pu[d].q0 = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d));
+        pu[d].q1 = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d) + 16);
+        pg[d].s = reinterpret_cast<const float*>(gs)[cb + d];
+        pu[d].s = reinterpret_cast<const float*>(us)[cb + d];
+      } else {
+        pg[d].q = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d));
+        pu[d].q = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d));
+      }
     }
-    uint2 swg, swu;
-    if constexpr (FMT == FMT_NVFP4) {
-      swg = *reinterpret_cast<const uint2*>(gs + 8 * (cb + g));
-      swu = *reinterpret_cast<const uint2*>(us + 8 * (cb + g));
-    } else {
-      swg = make_uint2(*reinterpret_cast<const uint32_t*>(gs + 4 * (cb + g)), 0u);
-      swu = make_uint2(*reinterpret_cast<const uint32_t*>(us + 4 * (cb + g)), 0u);
-    }
-    const uint2 og = exchange_scales<FMT>(swg, sm.sx[wave][0], r, g);
-    const uint2 ou = exchange_scales<FMT>(swu, sm.sx[wave][1], r, g);
+    if constexpr (!kFp8) {
+      uint2 swg, swu;
+      if constexpr (FMT == FMT_NVFP4) {
+        swg = *reinterpret_cast<const uint2*>(gs + 8 * (cb + g));
+        swu = *reinterpret_cast<const uint2*>(us + 8 * (cb + g));
+      } else {
+        swg = make_uint2(*reinterpret_cast<const uint32_t*>(gs + 4 * (cb + g)), 0u);
+        swu = make_uint2(*reinterpret_cast<const uint32_t*>(us + 4 * (cb + g)), 0u);
+      }
+      const uint2 og = exchange_scales<FMT>(swg, sm.sx[wave][0], r, g);
+      const uint2 ou = exchange_scales<FMT>(swu, sm.sx[wave][1], r, g);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      pg[d].s = scale_of_chunk<FMT>(og, d);
-      pu[d].s = scale_of_chunk<FMT>(ou, d);
+      for (int d = 0; d < 4; ++d) {
+        pg[d].s = scale_of_chunk<FMT>(og, d);
+        pu[d].s = scale_of_chunk<FMT>(ou, d);
+      }
     }
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < kB; ++d) {
       u32x4 bx[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         bx[i] = xr ? *reinterpret_cast<const u32x4*>(xr + 128 * (cb + d) + 32 * g + 8 * i)
                    : u32x4{0, 0, 0, 0};
-      ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pg[d]), as_bf16x8(bx[0]), ag, 0, 0, 0);
-      au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pu[d]), as_bf16x8(bx[0]), au, 0, 0, 0);
-      ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pg[d]), as_bf16x8(bx[1]), ag, 0, 0, 0);
-      au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pu[d]), as_bf16x8(bx[1]), au, 0, 0, 0);
-      ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pg[d]), as_bf16x8(bx[2]), ag, 0, 0, 0);
-      au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pu[d]), as_bf16x8(bx[2]), au, 0, 0, 0);
-      ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pg[d]), as_bf16x8(bx[3]), ag, 0, 0, 0);
-      au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pu[d]), as_bf16x8(bx[3]), au, 0, 0, 0);
+      // FP8: each chunk's sum starts from zero and is scaled by its block scale
+      f32x4 tg = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : ag, tu = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : au;
+      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pg[d]), as_bf16x8(bx[0]), tg, 0, 0, 0);
+      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pu[d]), as_bf16x8(bx[0]), tu, 0, 0, 0);
+      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pg[d]), as_bf16x8(bx[1]), tg, 0, 0, 0);
+      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pu[d]), as_bf16x8(bx[1]), tu, 0, 0, 0);
+      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pg[d]), as_bf16x8(bx[2]), tg, 0, 0, 0);
+      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pu[d]), as_bf16x8(bx[2]), tu, 0, 0, 0);
+      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pg[d]), as_bf16x8(bx[3]), tg, 0, 0, 0);
+      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pu[d]), as_bf16x8(bx[3]), tu, 0, 0, 0);
+      if constexpr (kFp8) {
+        ag = ag + pg[d].s * tg;
+        au = au + pu[d].s * tu;
+      } else {
+        ag = tg;
+        au = tu;
+      }
     }
   }
   // the four K quarters, summed in order
@@ -358,50 +391,71 @@ __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const
   uint16_t hv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) hv[j] = f32_to_bf16(silu_fast(sg[j] * tsg) * (su[j] * tsu));
-  uint16_t* o = a.h + (size_t)pairs[r] * I + n0 + 4 * g;
+  uint16_t* o = SHARED ? a.hs + (size_t)r * I + n0 + 4 * g : a.h + (size_t)pairs[r] * I + n0 + 4 * g;
   *reinterpret_cast<uint2*>(o) =
       make_uint2(hv[0] | (uint32_t(hv[1]) << 16), hv[2] | (uint32_t(hv[3]) << 16));
 }
 
-template <int RFMT, int SFMT>
+// The shared expert runs the lean tile too when its format has one and its
+// scale rows are whole-chunk words (FP4) or its block scales are per 128 K
+// (FP8); other formats keep the generic kernel.
+template <int SFMT>
+constexpr bool kSharedLean = SFMT == 0 || SFMT == FMT_NVFP4 || SFMT == FMT_MXFP4 || SFMT == FMT_FP8;
+
+template <int SFMT>
+__host__ __device__ __forceinline__ bool shared_lean_fits(const DecodeArgs& a) {
+  if constexpr (SFMT == FMT_NVFP4 || SFMT == FMT_MXFP4) return a.sg.wide && a.su.wide;
+  else return kSharedLean<SFMT>;
+}
+
+// LEAN: every block runs the aligned tile (routed FP4 experts, and the shared
+// expert when it has one), so the kernel holds none of the generic tile's
+// registers: 104 VGPRs instead of 236, four workgroups per CU instead of two.
+template <int RFMT, int SFMT, bool LEAN>
 __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs a) {
-  __shared__ GemvSmem<1, kGuWK, 2> sm;
   __shared__ GroupSmem grp;
   // The shared expert's gate/up blocks (independent of routing) come first.
   const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
-  if ((int)blockIdx.x < nsg) {
-    if constexpr (SFMT != 0) {
-      GemvIO io{a.x, a.hs, nullptr, a.k, kInShared, a.T};
-      gemv_tile<SFMT, kOpGateUp, 1, kGuWK>(a.sg, a.su, io, GemvRows{0, 0, a.T, nullptr, nullptr},
-                                           blockIdx.x, sm);
-    }
-    return;
-  }
   const int ntiles = a.I / gemv_rows_per_block<kOpGateUp>();
-  const int b = blockIdx.x - nsg;
-  const int q = b / ntiles, tile = b % ntiles;
-  extern __shared__ __attribute__((aligned(16))) char lean_dyn[];
-  LeanSmem& lsm = *reinterpret_cast<LeanSmem*>(lean_dyn);
-  constexpr bool kFp4 = RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4;
-  const bool lean = kFp4 && lean_fits(a);
-  if (kFp4 && lean && a.T == 1) lean_x_dma(a, lsm);
-  int e, n;
-  if (!derive_group(a, q, grp, e, n)) {
-    if (kFp4 && lean && a.T == 1) __builtin_amdgcn_s_waitcnt(0x0f70);  // no DMA outlives its block
-    return;
-  }
-  if constexpr (kFp4) {
-    if (lean) {
-      if (a.T == 1)
-        gate_up_lean<RFMT, true>(a, e, n, grp.toks, grp.pairs, tile, lsm);
-      else
-        gate_up_lean<RFMT, false>(a, e, n, grp.toks, grp.pairs, tile, lsm);
+  if constexpr (LEAN) {
+    static_assert((RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4) && kSharedLean<SFMT>, "lean tiles");
+    extern __shared__ __attribute__((aligned(16))) char lean_dyn[];
+    LeanSmem& lsm = *reinterpret_cast<LeanSmem*>(lean_dyn);
+    if ((int)blockIdx.x < nsg) {
+      if constexpr (SFMT != 0)
+        gate_up_lean<SFMT, false, true>(a, 0, a.T, nullptr, nullptr, blockIdx.x, lsm);
       return;
     }
+    const int b = blockIdx.x - nsg;
+    const int q = b / ntiles, tile = b % ntiles;
+    if (a.T == 1) lean_x_dma(a, lsm);
+    int e, n;
+    if (!derive_group(a, q, grp, e, n)) {
+      if (a.T == 1) __builtin_amdgcn_s_waitcnt(0x0f70);  // no DMA outlives its block
+      return;
+    }
+    if (a.T == 1)
+      gate_up_lean<RFMT, true, false>(a, e, n, grp.toks, grp.pairs, tile, lsm);
+    else
+      gate_up_lean<RFMT, false, false>(a, e, n, grp.toks, grp.pairs, tile, lsm);
+  } else {
+    __shared__ GemvSmem<1, kGuWK, 2> sm;
+    if ((int)blockIdx.x < nsg) {
+      if constexpr (SFMT != 0) {
+        GemvIO io{a.x, a.hs, nullptr, a.k, kInShared, a.T};
+        gemv_tile<SFMT, kOpGateUp, 1, kGuWK>(a.sg, a.su, io, GemvRows{0, 0, a.T, nullptr, nullptr},
+                                             blockIdx.x, sm);
+      }
+      return;
+    }
+    const int b = blockIdx.x - nsg;
+    const int q = b / ntiles, tile = b % ntiles;
+    int e, n;
+    if (!derive_group(a, q, grp, e, n)) return;
+    GemvIO io{a.x, a.h, nullptr, a.k, kInList, a.T};
+    gemv_tile<RFMT, kOpGateUp, 1, kGuWK>(a.gate, a.up, io, GemvRows{e, 0, n, grp.toks, grp.pairs},
+                                         tile, sm);
   }
-  GemvIO io{a.x, a.h, nullptr, a.k, kInList, a.T};
-  gemv_tile<RFMT, kOpGateUp, 1, kGuWK>(a.gate, a.up, io, GemvRows{e, 0, n, grp.toks, grp.pairs},
-                                       tile, sm);
 }
 
 // One 16-row tile (weight rows n0..n0+15 of expert e) times one bf16 input
@@ -564,11 +618,16 @@ struct GateUpLaunch {
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
     const int nsg = (SFMT != 0) ? a.I_shared / gemv_rows_per_block<kOpGateUp>() : 0;
     const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
-    // the aligned FP4 tile's LDS: reductions, scale exchange, T input rows
-    const bool lean = (RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4) && lean_fits(a);
-    const size_t dyn = lean ? offsetof(LeanSmem, x) + (size_t)a.T * a.H * 2 : 0;
-    return launch(decode_gateup_kernel<RFMT, SFMT>, dim3(nsg + ngu), dim3(kWave * kGuWK), dyn, s,
-                  a);
+    if constexpr ((RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4) && kSharedLean<SFMT>) {
+      if (lean_fits(a) && shared_lean_fits<SFMT>(a)) {
+        // the aligned tile's LDS: reductions, scale exchange, T input rows
+        const size_t dyn = offsetof(LeanSmem, x) + (size_t)a.T * a.H * 2;
+        return launch(decode_gateup_kernel<RFMT, SFMT, true>, dim3(nsg + ngu), dim3(kWave * kGuWK),
+                      dyn, s, a);
+      }
+    }
+    return launch(decode_gateup_kernel<RFMT, SFMT, false>, dim3(nsg + ngu), dim3(kWave * kGuWK), 0,
+                  s, a);
   }
 };
 
