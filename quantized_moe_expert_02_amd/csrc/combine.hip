@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       pp[b] = -1;
       wj[b] = 0.f;
       if (j0 + b < k) {  // wave-uniform
-        pp[b] = p2p[(size_t)t * k + j0 + b];
+        pp[b] = p2p ? p2p[(size_t)t * k + j0 + b] : t * k + j0 + b;
         wj[b] = w[(size_t)t * k + j0 + b];
       }
     }

@@ -458,6 +458,123 @@ __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs
   }
 }
 
+// ---- down projection per expert (2 to 8 tokens) ------------------------------
+// A block takes 64 output rows (four wavefronts of 16) of one expert's down
+// projection over all of K = I, for every row of the expert's group (the
+// group's h rows staged in LDS are the MFMA's B operand), so each expert's
+// weights are read once for all of its tokens (per-token blocks read a
+// popular expert once per token).  y rows go to memory in pair order; the
+// combine launch adds them in slot order.  The shared expert's blocks come
+// first (all T tokens, y_s).  FP4: batches of four 128-K chunks with the
+// whole-chunk scale words; FP8 block-128: batches of two, block scale per
+// chunk partial.
+constexpr int kDnRows = 16 * kGuWK;  // output rows per block
+
+template <int FMT>
+__host__ __device__ __forceinline__ bool down_lean_fits(const WDesc& w, int K, int H) {
+  if (H % kDnRows != 0 || K > kLeanMaxK) return false;
+  if constexpr (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) return w.wide && K % 512 == 0;
+  else return FMT == FMT_FP8 && K % 256 == 0;
+}
+
+template <int FMT, bool SHARED>
+__device__ inline void down_lean(const DecodeArgs& a, int e, int nrows, const int* pairs, int tile,
+                                 LeanSmem& sm) {
+  static_assert(FMT == FMT_NVFP4 || FMT == FMT_MXFP4 || FMT == FMT_FP8, "lean layouts");
+  constexpr bool kFp8 = FMT == FMT_FP8;
+  const WDesc& dw = SHARED ? a.sd : a.down;
+  const int K = SHARED ? a.I_shared : a.I, H = a.H;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int r = lane & 15, g = lane >> 4;
+  // the group's h rows into LDS (16-byte pieces, every thread)
+  for (int i = threadIdx.x * 8; i < nrows * K; i += kWave * kGuWK * 8) {
+    const int row = i / K, k = i - row * K;
+    const uint16_t* src = SHARED ? a.hs + (size_t)row * K : a.h + (size_t)pairs[row] * K;
+    *reinterpret_cast<u32x4*>(&sm.x[i]) = *reinterpret_cast<const u32x4*>(src + k);
+  }
+  const int n0 = tile * kDnRows + 16 * wave;
+  const int rb = kFp8 ? K : K / 2;
+  constexpr int cbytes = kFp8 ? 128 : 64;
+  constexpr int lbytes = kFp8 ? 32 : 16;
+  const uint8_t* wq = dw.codes + e * dw.stride_codes + (size_t)(n0 + r) * rb + lbytes * g;
+  const uint8_t* ws = scale_row_ptr<FMT>(dw, e, n0 + r);
+  float ts = 1.0f;
+  if constexpr (FMT == FMT_NVFP4) ts = dw.tscale[e];
+  __syncthreads();  // h staged
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* hr = (r < nrows) ? sm.x + r * K : nullptr;
+  constexpr int kB = kFp8 ? 2 : 4;
+  const int nch = K / 128;
+  for (int cb = 0; cb < nch; cb += kB) {
+    ARaw<FMT> pw[kB];
+#pragma unroll
+    for (int d = 0; d < kB; ++d) {
+      if constexpr (kFp8) {
+        pw[d].q0 = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d));
+        pw[d].q1 = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d) + 16);
+        pw[d].s = reinterpret_cast<const float*>(ws)[cb + d];
+      } else {
+        pw[d].q = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d));
+      }
+    }
+    if constexpr (!kFp8) {
+      uint2 sw;
+      if constexpr (FMT == FMT_NVFP4)
+        sw = *reinterpret_cast<const uint2*>(ws + 8 * (cb + g));
+      else
+        sw = make_uint2(*reinterpret_cast<const uint32_t*>(ws + 4 * (cb + g)), 0u);
+      const uint2 o = exchange_scales<FMT>(sw, sm.sx[wave][0], r, g);
+#pragma unroll
+      for (int d = 0; d < kB; ++d) pw[d].s = scale_of_chunk<FMT>(o, d);
+    }
+#pragma unroll
+    for (int d = 0; d < kB; ++d) {
+      u32x4 bx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bx[i] = hr ? *reinterpret_cast<const u32x4*>(hr + 128 * (cb + d) + 32 * g + 8 * i)
+                   : u32x4{0, 0, 0, 0};
+      f32x4 t = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc;
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pw[d]), as_bf16x8(bx[0]), t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pw[d]), as_bf16x8(bx[1]), t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pw[d]), as_bf16x8(bx[2]), t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pw[d]), as_bf16x8(bx[3]), t, 0, 0, 0);
+      if constexpr (kFp8)
+        acc = acc + pw[d].s * t;
+      else
+        acc = t;
+    }
+  }
+  if (r >= nrows) return;
+  // lane (r, g): output rows n0 + 4g + j of group row r
+  float* o = SHARED ? a.ys + (size_t)r * H + n0 + 4 * g : a.y + (size_t)pairs[r] * H + n0 + 4 * g;
+  *reinterpret_cast<f32x4*>(o) = acc * ts;
+}
+
+template <int RFMT, int SFMT>
+__global__ __launch_bounds__(kWave * kGuWK) void decode_down_kernel(DecodeArgs a) {
+  __shared__ GroupSmem grp;
+  extern __shared__ __attribute__((aligned(16))) char lean_dyn[];
+  LeanSmem& lsm = *reinterpret_cast<LeanSmem*>(lean_dyn);
+  const int ntiles = a.H / kDnRows;
+  const int nsd = (SFMT != 0) ? ntiles : 0;
+  if ((int)blockIdx.x < nsd) {
+    if constexpr (SFMT != 0) down_lean<SFMT, true>(a, 0, a.T, nullptr, blockIdx.x, lsm);
+    return;
+  }
+  const int b = blockIdx.x - nsd;
+  const int q = b / ntiles, tile = b % ntiles;
+  int e, n;
+  if (!derive_group(a, q, grp, e, n)) {
+    // a slot with no expert (id out of range) contributes zeros to the combine
+    if ((unsigned)a.ids[q] >= (unsigned)a.E && (int)threadIdx.x < kDnRows / 4)
+      *reinterpret_cast<f32x4*>(a.y + (size_t)q * a.H + tile * kDnRows + 4 * threadIdx.x) =
+          f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  down_lean<RFMT, false>(a, e, n, grp.pairs, tile, lsm);
+}
+
 // One 16-row tile (weight rows n0..n0+15 of expert e) times one bf16 input
 // row of length K, for the calling wavefront.  The weights are decoded in
 // registers as in gemv_tile; the input row is the MFMA's B operand column 0.
@@ -631,9 +748,31 @@ struct GateUpLaunch {
   }
 };
 
+// The per-expert down launch and the combine, for 2 to 8 tokens when the
+// down projections have lean tiles and the y buffers are given.
+template <int RFMT, int SFMT>
+constexpr bool kDownLean = (RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4 || RFMT == FMT_FP8) &&
+                           (SFMT == 0 || SFMT == FMT_NVFP4 || SFMT == FMT_MXFP4 || SFMT == FMT_FP8);
+
 struct DownLaunch {
   template <int RFMT, int SFMT>
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
+    if constexpr (kDownLean<RFMT, SFMT>) {
+      const bool fits = a.T >= 2 && a.y != nullptr && (SFMT == 0 || a.ys != nullptr) &&
+                        down_lean_fits<RFMT>(a.down, a.I, a.H) &&
+                        (SFMT == 0 || down_lean_fits<SFMT>(a.sd, a.I_shared, a.H));
+      if (fits) {
+        const int ntiles = a.H / kDnRows;
+        const int nsd = (SFMT != 0) ? ntiles : 0;
+        const int kmax = std::max(a.I, (SFMT != 0) ? a.I_shared : 0);
+        const size_t dyn = offsetof(LeanSmem, x) + (size_t)a.T * kmax * 2;
+        hipError_t err = launch(decode_down_kernel<RFMT, SFMT>, dim3(nsd + a.T * a.k * ntiles),
+                                dim3(kWave * kGuWK), dyn, s, a);
+        if (err != hipSuccess) return err;
+        return launch_combine(a.y, a.w, nullptr, (SFMT != 0) ? a.ys : nullptr, a.T, a.k, a.H, a.out,
+                              s);
+      }
+    }
     // One wavefront per slot (one round trip per block) when the grid is
     // smaller than the GPU; otherwise 8 per block keep more blocks resident.
     const int nslots = a.k + ((SFMT != 0) ? 1 : 0);

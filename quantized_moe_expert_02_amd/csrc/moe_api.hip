@@ -479,6 +479,8 @@ int32_t layer_impl(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16
     a.w = w;
     a.h = at<uint16_t>(ws, p.h);
     a.hs = L->has_shared ? at<uint16_t>(ws, p.hs) : nullptr;
+    a.y = at<float>(ws, p.y);
+    a.ys = L->has_shared ? at<float>(ws, p.ys) : nullptr;
     a.out = out;
     return hip_status(routed ? launch_decode_experts(a, s) : launch_decode(a, s));
   }

@@ -162,6 +162,8 @@ struct DecodeArgs {
   uint16_t* hs;       // [T][I_shared]
   uint16_t* out;      // [T][H]
   int dc_stage_k;     // down-combine launch: input rows staged in LDS, per-wave row length (0: not)
+  float* y;           // [T*k][H] fp32 partials (row = pair t*k+j) for the per-expert down, or nullptr
+  float* ys;          // [T][H] fp32 shared expert's down output, or nullptr
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Routing alone with the decode router (128-row slices, token groups of 8)
@@ -179,6 +181,7 @@ hipError_t launch_table_route(const int* tok, const int* table, int V, int T, in
                               const float* logits, int renorm, int* ids, float* w, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------------
+// pair_to_perm nullptr: y rows are in pair order (row t*k+j).
 hipError_t launch_combine(const float* y, const float* w, const int* pair_to_perm, const float* ys,
                           int T, int k, int H, uint16_t* out, hipStream_t s);
 
