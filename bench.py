@@ -481,15 +481,26 @@ def pmc_summarize(workload, mode, fetch_dir, write_dir):
 
 
 def cpu_model() -> str:
+    """The host CPU's model name with its family / model / stepping numbers
+    (some virtualised hosts report only a short name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if fields:
+                        break  # first processor only
+                    continue
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v
     except OSError:  # pragma: no cover
         pass
-    import platform
-    return platform.processor() or "unknown"
+    if "model name" not in fields:
+        import platform
+        return platform.processor() or "unknown"
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{fields['model name']} ({ids})" if ids else fields["model name"]
 
 
 def cpu_baseline(w, L, x_bits, budget_s, mode=None):
