@@ -271,7 +271,8 @@ __device__ __forceinline__ void lean_x_dma(const DecodeArgs& a, LeanSmem& sm) {
                                              0);
 }
 
-// XDMA: the input row is already on its way by lean_x_dma (one token).
+// XDMA: the input row is already on its way by lean_x_dma (one token);
+// else the rows are moved here.
 // SHARED: the shared expert (weights sg / su, expert 0, input rows = all T
 // tokens, output row t of hs); else routed expert e's group (rows toks[],
 // output rows pairs[] of h).  FP8 (block-128) chunks carry 32 codes per lane
@@ -286,13 +287,18 @@ __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const
   const int H = a.H, I = SHARED ? a.I_shared : a.I;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
-  // the group's input rows into LDS (16-byte pieces, every thread)
+  // the group's input rows into LDS by DMA (1 KiB per wavefront
+  // instruction, no register round trip): 8-token layers -0.25 us (NVFP4),
+  // -0.7 us (MXFP4) against 16-byte loads through registers
   if constexpr (!XDMA) {
-    for (int i = threadIdx.x * 8; i < nrows * H; i += kWave * kGuWK * 8) {
-      const int row = i / H, k = i - row * H;
-      const int tok = SHARED ? row : toks[row];
-      *reinterpret_cast<u32x4*>(&sm.x[i]) =
-          *reinterpret_cast<const u32x4*>(a.x + (size_t)tok * H + k);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.x), (short)0, a.T * H * 2, 0x00020000);
+    const int ppr = H / (kWave * 8);  // DMA instructions per row
+    for (int ii = wave; ii < nrows * ppr; ii += kGuWK) {
+      const int row = ii / ppr, piece = ii - row * ppr;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_ptr_t)(sm.x + row * H + piece * kWave * 8), 16,
+          2 * ((SHARED ? row : toks[row]) * H + piece * kWave * 8) + 16 * lane, 0, 0, 0);
     }
   }
   const int n0 = tile * 16;
@@ -310,7 +316,7 @@ __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const
     tsg = gw.tscale[e];
     tsu = uw.tscale[e];
   }
-  if constexpr (XDMA) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();  // x staged
   f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
   const uint16_t* xr = (r < nrows) ? sm.x + r * H : nullptr;
@@ -472,9 +478,10 @@ constexpr int kDnRows = 16 * kGuWK;  // output rows per block
 
 template <int FMT>
 __host__ __device__ __forceinline__ bool down_lean_fits(const WDesc& w, int K, int H) {
-  if (H % kDnRows != 0 || K > kLeanMaxK) return false;
-  if constexpr (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) return w.wide && K % 512 == 0;
-  else return FMT == FMT_FP8 && K % 256 == 0;
+  // whole 512-value DMA pieces per h row; FP4 loads in batches of four chunks
+  if (H % kDnRows != 0 || K > kLeanMaxK || K % 512 != 0) return false;
+  if constexpr (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) return w.wide;
+  else return FMT == FMT_FP8;
 }
 
 template <int FMT, bool SHARED>
@@ -486,11 +493,20 @@ __device__ inline void down_lean(const DecodeArgs& a, int e, int nrows, const in
   const int K = SHARED ? a.I_shared : a.I, H = a.H;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
-  // the group's h rows into LDS (16-byte pieces, every thread)
-  for (int i = threadIdx.x * 8; i < nrows * K; i += kWave * kGuWK * 8) {
-    const int row = i / K, k = i - row * K;
-    const uint16_t* src = SHARED ? a.hs + (size_t)row * K : a.h + (size_t)pairs[row] * K;
-    *reinterpret_cast<u32x4*>(&sm.x[i]) = *reinterpret_cast<const u32x4*>(src + k);
+  // the group's h rows into LDS by DMA (1 KiB per wavefront instruction)
+  {
+    const uint16_t* base = SHARED ? a.hs : a.h;
+    const int nsrc = SHARED ? a.T : a.T * a.k;  // rows of the source buffer
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base), (short)0, nsrc * K * 2, 0x00020000);
+    const int ppr = K / (kWave * 8);  // DMA instructions per row
+    for (int ii = wave; ii < nrows * ppr; ii += kGuWK) {
+      const int row = ii / ppr, piece = ii - row * ppr;
+      const int srow = SHARED ? row : pairs[row];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(sm.x + row * K + piece * kWave * 8),
+                                               16, 2 * (srow * K + piece * kWave * 8) + 16 * lane,
+                                               0, 0, 0);
+    }
   }
   const int n0 = tile * kDnRows + 16 * wave;
   const int rb = kFp8 ? K : K / 2;
@@ -500,6 +516,7 @@ __device__ inline void down_lean(const DecodeArgs& a, int e, int nrows, const in
   const uint8_t* ws = scale_row_ptr<FMT>(dw, e, n0 + r);
   float ts = 1.0f;
   if constexpr (FMT == FMT_NVFP4) ts = dw.tscale[e];
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();  // h staged
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t* hr = (r < nrows) ? sm.x + r * K : nullptr;
