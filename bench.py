@@ -390,7 +390,11 @@ def dominant_kernel_name(w, mode="exact"):
     fmt = codes[w.fmt]
     if w.T <= DECODE_ROWS:
         sfmt = codes[w.shared_fmt] if w.I_shared else 0
-        return f"decode_gateup_kernel<{fmt}, {sfmt}>"
+        # the register-lean instance when every tile of the launch has an
+        # aligned FP4 (routed) / FP4 or FP8 (shared) form
+        lean = (w.fmt in ("nvfp4", "mxfp4") and sfmt in (0, 1, 2, 3)
+                and w.H % 2048 == 0 and w.H <= 4096)
+        return f"decode_gateup_kernel<{fmt}, {sfmt}, {'true' if lean else 'false'}>"
     if w.T <= GEMV_MAX_ROWS:
         base = "expert_gemv_kernel"
     elif w.fmt in ("nvfp4", "mxfp4") and w.H % 64 == 0:

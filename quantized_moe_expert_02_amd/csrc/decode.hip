@@ -5,7 +5,7 @@
 // the weights at the memory's line rate).  On gfx950 a dependent kernel in the
 // same stream starts about 1.5 us after its predecessor ends, while a
 // cross-workgroup hand-off inside a kernel needs an agent-scope release
-// (an L2 write-back) and costs far more; so the layer runs as four short
+// (an L2 write-back) and costs far more; so the layer runs as a few short
 // launches with no intra-kernel hand-off:
 //
 //   1. router partial sums over (128-row slice x 32 experts) blocks;
@@ -17,11 +17,15 @@
 //      block of an expert's first pair derives the expert's (token, slot)
 //      pairs from the <= 256 routed ids, the others exit); the first blocks
 //      compute the shared expert's gate/up + SwiGLU;
-//   4. per (token, 16 output columns): the down projections of the token's k
-//      slots and of the shared expert, combined in slot order in fp32 and
-//      rounded once to bf16.
+//   4. one token: per (token, 16 output columns), the down projections of
+//      the token's k slots and of the shared expert, combined in slot order
+//      in fp32 and rounded once to bf16;
+//      2 to 8 tokens: per (expert group, 64 output rows), the down projection
+//      once for all of the expert's tokens into fp32 y (pair order), then
+//   5. the slot-order combine (combine.hip).
 //
-// Rows of h are indexed by pair (t*k + j), so no permutation is needed.
+// Rows of h (and y) are indexed by pair (t*k + j), so no permutation is
+// needed.
 #include "gemv_core.cuh"
 #include "topk_core.cuh"
 
