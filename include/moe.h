@@ -208,8 +208,11 @@ int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pai
  * fp32 [T][E], ids int32 [T][k], weights fp32 [T][k].  The lowering follows
  * the row count (gitee "dgpp" README, "Highlights": row-aware execution):
  * T <= 8 runs the decode lowering (each active expert's weights streamed once
- * for all its tokens), 9..64 the expert GEMV, larger T the grouped GEMM over
- * a tile list.  Errors: MOE_ERR_INVALID_ARG (T < 0, null or misaligned x /
+ * for all its tokens), and so does T <= 16 with T*k <= 256 when every
+ * projection has the aligned tile (FP4 gate/up with H a multiple of 2048 and
+ * H <= 4096; FP4 or FP8 down projections with I a multiple of 512, I <= 4096
+ * and H a multiple of 64; whole-chunk FP4 scale words); otherwise 9..64 rows
+ * run the expert GEMV, larger T the grouped GEMM over a tile list.  Errors: MOE_ERR_INVALID_ARG (T < 0, null or misaligned x /
  * out), MOE_ERR_WORKSPACE (ws null, misaligned or below
  * moe_workspace_size(L, T)), MOE_ERR_UNSUPPORTED (a shape or format the
  * descriptor check rejects), MOE_ERR_HIP (a launch failed; moe_last_error
@@ -311,8 +314,8 @@ int32_t moe_route_table(const moe_layer_desc* L, const uint16_t* x, float* logit
 /* moe_layer_forward_ex on a given routing (topk_ids int32 [T][k], topk_w fp32
  * [T][k], device, e.g. from moe_route_topk or moe_route_table) instead of the
  * router: grouping, experts, shared expert and combine.  Expert ids outside
- * [0, E) are dropped (their slots contribute nothing).  For T <= 8 only the
- * fused decode's two expert launches run. */
+ * [0, E) are dropped (their slots contribute nothing).  Where
+ * moe_layer_forward takes the decode lowering only its expert launches run. */
 int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int32_t T,
                                  const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                                  void* ws, size_t ws_bytes, int32_t act_mode, void* stream);
@@ -327,8 +330,8 @@ int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int
  *            e = topk_ids[t][j] (rows of skipped pairs are not written);
  *   h_shared bf16 [T][I_shared] (the shared expert), NULL without one.
  * T > 8 returns MOE_ERR_UNSUPPORTED.  This is the first of the decode
- * lowering's two expert launches, exposed so that it can be timed and
- * checked on its own; moe_layer_forward runs it for T <= 8. */
+ * lowering's expert launches, exposed so that it can be timed and checked on
+ * its own; moe_layer_forward runs it wherever it takes the decode lowering. */
 int32_t moe_decode_gate_up(const moe_layer_desc* L, const uint16_t* x, int32_t T,
                            const int32_t* topk_ids, uint16_t* h, uint16_t* h_shared, void* stream);
 

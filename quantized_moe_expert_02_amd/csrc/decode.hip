@@ -1,4 +1,5 @@
-// Decode lowering (T <= 8 rows) of the whole layer.
+// Decode lowering (T <= 8 rows; up to 16 where every launch has its aligned
+// tile) of the whole layer.
 //
 // Decode is a weight-streaming problem (forum thread "DGPP: a GB10-optimized
 // C++/CUDA inference engine", the "Lossless bf12" post: decode kernels read
@@ -20,8 +21,9 @@
 //   4. one token: per (token, 16 output columns), the down projections of
 //      the token's k slots and of the shared expert, combined in slot order
 //      in fp32 and rounded once to bf16;
-//      2 to 8 tokens: per (expert group, 64 output rows), the down projection
-//      once for all of the expert's tokens into fp32 y (pair order), then
+//      2 to 16 tokens: per (expert group, 64 output rows), the down
+//      projection once for all of the expert's tokens into fp32 y (pair
+//      order), then
 //   5. the slot-order combine (combine.hip).
 //
 // Rows of h (and y) are indexed by pair (t*k + j), so no permutation is
@@ -242,9 +244,9 @@ constexpr int kGuWK = GemvShape<kOpGateUp>::WK;  // K split of the gate/up tiles
 // per-load bounds test: wavefront w takes the contiguous K quarter
 // [w K/4, (w+1) K/4) in whole batches of four 128-K chunks, every lane's loads of a
 // batch share one base address per matrix (immediate offsets), the group's
-// input rows (at most 8 tokens) are staged once in LDS and read from there
+// input rows (at most 16 tokens) are staged once in LDS and read from there
 // as the MFMA B operand, and the four quarters are summed in a fixed order.
-constexpr int kLeanMaxRows = kTmax;
+constexpr int kLeanMaxRows = 16;  // the MFMA B operand's 16 columns
 constexpr int kLeanMaxK = 4096;
 
 struct LeanSmem {
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs
   }
 }
 
-// ---- down projection per expert (2 to 8 tokens) ------------------------------
+// ---- down projection per expert (2 to 16 tokens) -----------------------------
 // A block takes 64 output rows (four wavefronts of 16) of one expert's down
 // projection over all of K = I, for every row of the expert's group (the
 // group's h rows staged in LDS are the MFMA's B operand), so each expert's
@@ -769,7 +771,7 @@ struct GateUpLaunch {
   }
 };
 
-// The per-expert down launch and the combine, for 2 to 8 tokens when the
+// The per-expert down launch and the combine, for 2 to 16 tokens when the
 // down projections have lean tiles and the y buffers are given.
 template <int RFMT, int SFMT>
 constexpr bool kDownLean = (RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4 || RFMT == FMT_FP8) &&
@@ -836,6 +838,26 @@ hipError_t by_formats(int rfmt, int sfmt, const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool decode_rows_ok(const DecodeArgs& a) {
+  if (a.T <= kTmax) return true;
+  // 9..16 rows: only the lean gate/up and the per-expert down, whose groups
+  // fill at most the 16 columns of the MFMA B operand; pair slots <= 256
+  // (one thread per slot in derive_group)
+  if (a.T > kLeanMaxRows || a.T * a.k > kPmax) return false;
+  if (!(a.gate.fmt == FMT_NVFP4 || a.gate.fmt == FMT_MXFP4) || !lean_fits(a)) return false;
+  if (a.has_shared) {
+    const int f = a.sg.fmt;
+    if (!(f == FMT_FP8 || ((f == FMT_NVFP4 || f == FMT_MXFP4) && a.sg.wide && a.su.wide)))
+      return false;
+  }
+  auto down_ok = [&](const WDesc& w, int K) {
+    if (a.H % kDnRows != 0 || K > kLeanMaxK || K % 512 != 0) return false;
+    return ((w.fmt == FMT_NVFP4 || w.fmt == FMT_MXFP4) && w.wide) || w.fmt == FMT_FP8;
+  };
+  if (!down_ok(a.down, a.I) || (a.has_shared && !down_ok(a.sd, a.I_shared))) return false;
+  return a.y != nullptr && (!a.has_shared || a.ys != nullptr);
+}
 
 DecodePlan decode_plan(int T, int H, int E) {
   DecodePlan p;

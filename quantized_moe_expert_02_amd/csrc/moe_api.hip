@@ -147,7 +147,7 @@ struct WsPlan {
   // matrix-core router (T > kGemvMaxRows): split router planes and w^2 sums
   bool mfma_router;
   size_t planes, wrt, wsq;
-  // fused decode (T <= kDecodeRows): router slice sums
+  // decode router (T <= kRouterSlicedRows): slice sums
   size_t dpart, dapart;
   // lossy activation modes (T > kGemvMaxRows): quantized x, h and shared h
   // (codes sized for E4M3, scales 4 bytes per 128 K per row)
@@ -470,7 +470,7 @@ int32_t layer_impl(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16
   // (the kernels only read a given routing)
   int* ids = routed ? const_cast<int*>(given_ids) : (dbg_ids ? dbg_ids : at<int>(ws, p.ids));
   float* w = routed ? const_cast<float*>(given_w) : (dbg_w ? dbg_w : at<float>(ws, p.w));
-  if (T <= kDecodeRows) {
+  if (T <= kDecodeMaxRows) {
     DecodeArgs a = decode_args(L, x, T, p);
     a.part = at<float>(ws, p.dpart);
     a.apart = at<float>(ws, p.dapart);
@@ -482,7 +482,8 @@ int32_t layer_impl(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16
     a.y = at<float>(ws, p.y);
     a.ys = L->has_shared ? at<float>(ws, p.ys) : nullptr;
     a.out = out;
-    return hip_status(routed ? launch_decode_experts(a, s) : launch_decode(a, s));
+    if (decode_rows_ok(a))  // else the 9-64-row lowering below
+      return hip_status(routed ? launch_decode_experts(a, s) : launch_decode(a, s));
   }
   if (!routed && (st = run_route(L, x, dbg_logits, T, ids, w, ws, p, s)) != MOE_OK) return st;
   int* offsets = at<int>(ws, p.offsets);

@@ -81,6 +81,40 @@ def test_layer_decode_full(name):
         f"unique experts={len(np.unique(r['ids']))}")
 
 
+# 9 to 16 rows with the aligned (lean) tiles in every launch: the decode
+# lowering (decode router, block top-k, per-group gate/up, per-expert down,
+# combine) with expert groups of up to 16 rows, the MFMA B operand's width.
+DECODE_ROWS = {
+    # k = E: every group holds all 16 tokens
+    "nvfp4_t16_full_groups": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t16_full_groups", T=16,
+                                          H=2048, E=4, I=512, top_k=4, I_shared=512,
+                                          shared_fmt=synth.FMT_NVFP4),
+    "mxfp4_t9_k4096": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp4_t9_k4096", T=9, H=4096, E=10,
+                                   I=512, top_k=2, fmt=synth.FMT_MXFP4, I_shared=1024,
+                                   shared_fmt=synth.FMT_FP8, zipf_s=1.1),
+    "nvfp4_t13_fp8_down": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t13_fp8_down", T=13,
+                                       H=2048, E=12, I=1024, top_k=3, fmt=synth.FMT_NVFP4,
+                                       down_fmt=synth.FMT_FP8, I_shared=512,
+                                       shared_fmt=synth.FMT_FP8,
+                                       shared_down_fmt=synth.FMT_NVFP4, zipf_s=1.1),
+    "decode_t16_nvfp4_zipf": synth.scaled(W["decode_t8_nvfp4_zipf"], name="decode_t16_nvfp4_zipf",
+                                          T=16, weight_sets=1),
+    "decode_t12_mxfp4_zipf": synth.scaled(W["decode_t8_mxfp4_zipf"], name="decode_t12_mxfp4_zipf",
+                                          T=12, weight_sets=1),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_ROWS))
+def test_layer_decode_rows(name):
+    w = DECODE_ROWS[name]
+    say(f"[gpu] layer {name}: T={w.T} H={w.H} E={w.E} I={w.I} k={w.top_k} fmt={w.fmt}")
+    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), what=name)
+    counts = np.bincount(r["ids"].reshape(-1), minlength=w.E)
+    say(f"[gpu] layer {name}: rel={r['rel']:.2e} worst={r['worst']:.2e} max group={counts.max()}")
+    if w.top_k == w.E:
+        assert counts.max() == w.T
+
+
 # The 9-64 row band (speculative-verify and batched-decode sizes): sliced
 # router, block top-k, expert GEMV in 16-row passes (groups above 16 rows
 # under the Zipf router), shared expert over up to 4 passes.

@@ -84,6 +84,20 @@ def test_layer_on_table_routing(T):
     the table) through the fused decode, expert GEMV and grouped GEMM."""
     w = synth.scaled(W["tiny_nvfp4_t4"], name="tab_layer", T=150, H=352, E=12, I=160, top_k=3,
                      I_shared=96, shared_fmt=synth.FMT_FP8)
+    check_table_routed_layer(w, T)
+
+
+@pytest.mark.parametrize("T", [6, 13])
+def test_aligned_layer_on_table_routing(T):
+    """The same at a shape with aligned tiles in every decode launch (K a
+    multiple of 2048 for gate/up and of 512 for down): the per-expert down
+    projection zero-fills the rows of out-of-range slots, for up to 16 rows."""
+    w = synth.scaled(W["tiny_nvfp4_t4"], name="tab_aligned", T=16, H=2048, E=12, I=512, top_k=3,
+                     I_shared=512, shared_fmt=synth.FMT_NVFP4)
+    check_table_routed_layer(w, T)
+
+
+def check_table_routed_layer(w, T):
     L = layer_for(w)
     dl = device_layer(L)
     x_bits = synth.make_x(w)[:T]
