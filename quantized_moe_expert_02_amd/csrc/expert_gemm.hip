@@ -33,6 +33,8 @@ constexpr int BM = kGemmTileM, BN = 128, BK = 64;
 // conflict-free when the two threads of a row interleave their 16-byte pieces.
 constexpr int LDSW = BK + 16;
 constexpr int kXcds = 8;
+// Row tiles per run of the tile order (gemm_tile_order).
+constexpr int kRowRun = 4;
 
 struct GemmParams {
   WDesc w0, w1;           // gate, up (gate/up) or down (both)
@@ -123,16 +125,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   __shared__ GemmSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-aware order: workgroup b runs on XCD b % 8.  Each XCD takes a
-  // contiguous range of the live (row tile, column tile) pairs, column tiles
-  // fastest, so the column tiles of one row tile (same activation rows) and
-  // the row tiles of one expert (same weights) share that XCD's L2.
+  // contiguous range of the live (row tile, column tile) pairs in the order
+  // of gemm_tile_order (runs of up to four row tiles of one expert, row tiles
+  // fastest), so a run's workgroups share each weight column tile and its
+  // activation rows in that XCD's L2 (wide FP8 prefill gate/up 6.31 -> 6.15
+  // ms against column tiles fastest, its 1x128 mode 3.48 -> 3.22 ms).
   const int n_rt = (p.tiles == nullptr) ? (p.T + BM - 1) / BM : min(*p.n_tiles, p.max_rt);
   const int live = n_rt * p.ntn;
   const int per = (live + kXcds - 1) / kXcds;
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
   const int idx = xcd * per + local;
   if (local >= per || idx >= live) return;
-  const int mt = idx / p.ntn, nt = idx % p.ntn;
+  const int2 tn = gemm_tile_order(idx, p.ntn, n_rt, kRowRun, p.tiles, p.offsets, BM);
+  const int mt = tn.x, nt = tn.y;
   int e, m0, m1;
   if (p.tiles == nullptr) {  // shared expert over rows 0..T-1
     e = 0;

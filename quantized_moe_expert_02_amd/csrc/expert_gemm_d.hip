@@ -34,6 +34,8 @@ namespace {
 constexpr int BM = kGemmTileM, BN = 256, BK = 64;
 constexpr int kWaves = 4, kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
+// Row tiles per run of the tile order (gemm_tile_order).
+constexpr int kRowRun = 4;
 // Three stages of 24 KiB and two 4 KiB scale buffers: two steps in flight
 // while one is computed, and two workgroups per CU fill the 160 KiB of LDS.
 constexpr int kStages = 3;
@@ -165,7 +167,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
   const int idx = xcd * per + local;
   if (local >= per || idx >= live) return;
-  const int mt = idx / p.ntn, nt = idx % p.ntn;
+  const int2 tn = gemm_tile_order(idx, p.ntn, n_rt, kRowRun, p.tiles, p.offsets, BM);
+  const int mt = tn.x, nt = tn.y;
   int e, m0, m1;
   if (p.tiles == nullptr) {
     e = 0;

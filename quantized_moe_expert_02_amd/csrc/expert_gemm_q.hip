@@ -37,6 +37,8 @@ namespace {
 
 constexpr int BM = kGemmTileM, BN = 128, BK = 128;
 constexpr int kXcds = 8;
+// Row tiles per run of the tile order (gemm_tile_order).
+constexpr int kRowRun = 4;
 constexpr int kFmtFp8 = 0, kFmtFp4 = 4;  // operand format codes of the instruction
 
 // LDS rows hold one K step of one tile row in K order, then the row's scale
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
   const int idx = xcd * per + local;
   if (local >= per || idx >= live) return;
-  const int mt = idx / p.ntn, nt = idx % p.ntn;
+  const int2 tn = gemm_tile_order(idx, p.ntn, n_rt, kRowRun, p.tiles, p.offsets, BM);
+  const int mt = tn.x, nt = tn.y;
   int e, m0, m1;
   if (p.tiles == nullptr) {
     e = 0;
@@ -484,7 +487,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
   const int idx = xcd * per + local;
   if (local >= per || idx >= live) return;
-  const int mt = idx / p.ntn, nt = idx % p.ntn;
+  const int2 tn = gemm_tile_order(idx, p.ntn, n_rt, kRowRun, p.tiles, p.offsets, BM);
+  const int mt = tn.x, nt = tn.y;
   int e, m0, m1;
   if (p.tiles == nullptr) {
     e = 0;

@@ -90,6 +90,35 @@ __device__ __forceinline__ float wave_max_f(float v) {
   return v;
 }
 
+// Order of a grouped GEMM's (row tile, column tile) pairs.  The row tiles of
+// one expert are cut into runs of at most `run` consecutive tiles, and a run
+// takes every column tile with its row tiles fastest: the run's workgroups
+// read each weight column tile together (one HBM fetch per run, not one per
+// row tile) while its activation rows stay in L2.  idx in [0, n_rt * ntn)
+// maps one to one onto (row tile, column tile) in [0, n_rt) x [0, ntn); run
+// 1 is column tiles fastest.  tiles: int2 (expert, first permuted row) in
+// expert order, tile_m rows each, as the grouping writes them from offsets;
+// nullptr: one expert whose rows are all n_rt tiles.
+__device__ inline int2 gemm_tile_order(int idx, int ntn, int n_rt, int run, const int2* tiles,
+                                       const int* offsets, int tile_m) {
+  const int lin = idx / ntn;  // a row tile of idx's run
+  if (run <= 1) return make_int2(lin, idx - lin * ntn);
+  int j = lin, R = n_rt;  // lin's place among its expert's tiles, their count
+  if (tiles != nullptr) {
+    const int2 tl = tiles[lin];
+    const int a = offsets[tl.x], b = offsets[tl.x + 1];
+    if (tl.y < a || b <= tl.y) return make_int2(lin, idx - lin * ntn);  // not from these offsets
+    j = (tl.y - a) / tile_m;
+    R = (b - a + tile_m - 1) / tile_m;
+    if (j > lin) return make_int2(lin, idx - lin * ntn);
+  }
+  const int c = j / run;
+  const int start = lin - j + c * run;
+  const int size = min(min(run, R - c * run), n_rt - start);
+  const int rem = idx - start * ntn;
+  return make_int2(start + rem % size, rem / size);
+}
+
 // Launch a kernel and return the status of this launch alone (not the
 // thread's sticky last-error state, which other libraries may have left set).
 template <typename... KArgs, typename... Args, size_t... Is>
