@@ -34,8 +34,12 @@ namespace {
 constexpr int BM = kGemmTileM, BN = 256, BK = 64;
 constexpr int kWaves = 4, kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
-// Row tiles per run of the tile order (gemm_tile_order).
-constexpr int kRowRun = 4;
+// Row tiles per run of the tile order (gemm_tile_order): one, i.e. column
+// tiles fastest.  Runs of four left the 8192-token FP4 layers' time unchanged
+// and raised the gate/up launch's HBM bytes (NVFP4 1.14 -> 1.25 GB): with
+// K = 2048 the weights are reused within a run, but the activation rows of
+// the tiles in flight no longer fit the L2 together.
+constexpr int kRowRun = 1;
 // Three stages of 24 KiB and two 4 KiB scale buffers: two steps in flight
 // while one is computed, and two workgroups per CU fill the 160 KiB of LDS.
 constexpr int kStages = 3;
