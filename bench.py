@@ -9,9 +9,10 @@ captured HIP graph; inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is tokens/s over the timed steps, with
 p10/p50/p90 microseconds per layer over the graph replays.  The `roofline`
-object covers the dominant kernel, the gate/up kernel the layer runs (for
-T <= 8 the decode lowering's gate/up launch, routed and shared experts; the
-expert GEMV up to 64 rows; the grouped GEMM above): algorithmic bytes
+object covers the dominant kernel, the gate/up kernel the layer runs (the
+decode lowering's gate/up launch, routed and shared experts, for T <= 8 and
+for up to 32 rows on aligned shapes; else the expert GEMV up to 64 rows; the
+grouped GEMM above): algorithmic bytes
 (decode, HBM-bound) or flops (prefill, MFMA-bound) per launch over its
 average launch duration, measured with one pair of HIP events around a batch
 of back-to-back launches on the launch stream;
@@ -42,6 +43,30 @@ FP4_PEAK_TFLOPS = 10100.0
 FP8_PEAK_TFLOPS = 5000.0
 GEMV_MAX_ROWS = 64  # calls with more tokens run the tiled grouped GEMM
 DECODE_ROWS = 8     # calls with at most this many tokens run the decode lowering
+DECODE_MAX_ROWS = 32  # ... and up to this many when every launch has its aligned tile
+
+
+def decode_lowering(w):
+    """Whether moe_layer_forward runs the decode lowering for this workload
+    (the library's rule: T <= 8, or T <= 32 with T*k <= 512 when every
+    projection has the aligned tile)."""
+    if w.T <= DECODE_ROWS:
+        return True
+    if w.T > DECODE_MAX_ROWS or w.T * w.top_k > 512:
+        return False
+    fp4 = ("nvfp4", "mxfp4")
+    if w.fmt not in fp4 or w.H % 2048 != 0 or w.H > 4096 or w.H % 64 != 0:
+        return False
+    def down_ok(fmt, K):
+        return fmt in fp4 + ("fp8_b128",) and K % 512 == 0 and K <= 4096
+    if not down_ok(w.down_fmt or w.fmt, w.I):
+        return False
+    if w.I_shared:
+        if w.shared_fmt not in fp4 + ("fp8_b128",):
+            return False
+        if not down_ok(w.shared_down_fmt or w.shared_fmt, w.I_shared):
+            return False
+    return True
 
 # Opt-in lossy activation modes: (C code, arithmetic type, dense MFMA peak of
 # the operand pair in TFLOP/s).  An E4M3 x E2M1 pair runs at the FP8 rate.
@@ -223,7 +248,7 @@ def main():
     P = T * k
     offsets, p2, act, h = dominant_inputs(moe, torch, dev, L, ids)
     M = args.kernel_launches
-    launch_gate_up = dominant_launcher(moe, torch, dev, L, T, x, ids, offsets, p2, act, h, ws,
+    launch_gate_up = dominant_launcher(moe, torch, dev, L, w, x, ids, offsets, p2, act, h, ws,
                                        mode_code if lossy else 0)
     for i in range(min(M, 2 * nsets)):  # warm
         launch_gate_up(sets[i % nsets])
@@ -243,7 +268,8 @@ def main():
     k_avg_us = k0.elapsed_time(k1) * 1e3 / M
     active = np.unique(ids_np)
     k_bytes = len(active) * (expert_bytes(L.gate) + expert_bytes(L.up)) + T * L.H * 2 + P * L.I * 2
-    if T <= DECODE_ROWS and L.has_shared:
+    dec = decode_lowering(w) and not lossy
+    if dec and L.has_shared:
         # the decode gate/up launch computes the shared expert's gate/up too
         k_bytes += expert_bytes(L.sh_gate) + expert_bytes(L.sh_up) + T * L.I_shared * 2
     k_gbs = k_bytes / (k_avg_us * 1e-6) / 1e9
@@ -254,7 +280,7 @@ def main():
         f"{k_tflops:.1f} TFLOP/s")
     if T <= GEMV_MAX_ROWS:
         # weights streamed once per group: bound by HBM
-        what = (" (routed and shared gate/up + SwiGLU)" if T <= DECODE_ROWS and L.has_shared
+        what = (" (routed and shared gate/up + SwiGLU)" if dec and L.has_shared
                 else " (routed gate/up + SwiGLU)")
         roof = {"kernel": dominant_kernel_name(w, mode) + what,
                 "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -306,7 +332,7 @@ def main():
         "layer_fp4_mfma_frac": round(layer_tflops / FP4_PEAK_TFLOPS, 5),
         "unique_experts": int(len(active)),
         "routing_matches_oracle": routing_exact,
-        "roofline": dict(roof, traffic=load_traffic(w.name, T, mode if lossy else "exact")),
+        "roofline": dict(roof, traffic=load_traffic(w, mode if lossy else "exact")),
     }
 
     # ---- CPU baseline: the oracle on a bounded sample ----
@@ -332,12 +358,13 @@ def dominant_inputs(moe, torch, dev, L, ids):
     return offsets, p2, act, h
 
 
-def dominant_launcher(moe, torch, dev, L, T, x, ids, offsets, p2, act, h, ws, mode_code):
+def dominant_launcher(moe, torch, dev, L, w, x, ids, offsets, p2, act, h, ws, mode_code):
     """A function launching the gate/up kernel the layer runs, on one weight
-    set: the decode lowering's (T <= 8: routed and shared experts, on the
-    layer's routing), the expert GEMV or grouped GEMM's, or (lossy mode) the
+    set: the decode lowering's (routed and shared experts, on the layer's
+    routing), the expert GEMV or grouped GEMM's, or (lossy mode) the
     scaled-MFMA one on x quantized once."""
-    if T <= DECODE_ROWS and mode_code == 0:
+    T = w.T
+    if decode_lowering(w) and mode_code == 0:
         hp = torch.empty((T * L.top_k, L.I), dtype=torch.bfloat16, device=dev)
         hs = (torch.empty((T, L.I_shared), dtype=torch.bfloat16, device=dev)
               if L.has_shared else None)
@@ -366,7 +393,7 @@ def pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws, mode_code):
     the dominant kernel, cycling weight sets as the timed run does."""
     T = ids.shape[0]
     offsets, p2, act, h = dominant_inputs(moe, torch, dev, L, ids)
-    launch_gate_up = dominant_launcher(moe, torch, dev, L, T, x, ids, offsets, p2, act, h, ws,
+    launch_gate_up = dominant_launcher(moe, torch, dev, L, w, x, ids, offsets, p2, act, h, ws,
                                        mode_code)
     src = torch.ones(PMC_COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -388,7 +415,7 @@ def dominant_kernel_name(w, mode="exact"):
         return f"{base}<{ACT_MODES[mode][0]}, 0>"
     codes = {"nvfp4": 1, "mxfp4": 2, "fp8_b128": 3, "mxfp8": 4}
     fmt = codes[w.fmt]
-    if w.T <= DECODE_ROWS:
+    if decode_lowering(w):
         sfmt = codes[w.shared_fmt] if w.I_shared else 0
         # the register-lean instance when every tile of the launch has an
         # aligned FP4 (routed) / FP4 or FP8 (shared) form
@@ -404,10 +431,11 @@ def dominant_kernel_name(w, mode="exact"):
     return f"{base}<{fmt}, 0>"
 
 
-def dominant_sources(T, mode="exact"):
+def dominant_sources(w, mode="exact"):
     pkg = os.path.join(ROOT, "quantized_moe_expert_02_amd", "csrc")
     files = ["moe_device.cuh", "gemv_core.cuh"]
-    if T <= DECODE_ROWS:
+    T = w.T
+    if mode == "exact" and decode_lowering(w):
         files += ["decode.hip"]
     elif T <= GEMV_MAX_ROWS:
         files += ["expert_gemv.hip"]
@@ -416,10 +444,10 @@ def dominant_sources(T, mode="exact"):
     return [os.path.join(pkg, f) for f in files]
 
 
-def source_hash(T, mode="exact"):
+def source_hash(w, mode="exact"):
     import hashlib
     hsh = hashlib.sha256()
-    for f in dominant_sources(T, mode):
+    for f in dominant_sources(w, mode):
         with open(f, "rb") as fh:
             hsh.update(fh.read())
     return hsh.hexdigest()[:16]
@@ -430,15 +458,15 @@ def traffic_path(workload, mode="exact"):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
 
 
-def load_traffic(workload, T, mode="exact"):
+def load_traffic(w, mode="exact"):
     """Counter-measured HBM bytes per launch of the dominant kernel, if the
     counters were taken on the kernel sources as they are now; else None."""
-    p = traffic_path(workload, mode)
+    p = traffic_path(w.name, mode)
     if not os.path.exists(p):
         return None
     with open(p) as fh:
         t = json.load(fh)
-    if t.get("source_hash") != source_hash(T, mode):
+    if t.get("source_hash") != source_hash(w, mode):
         return None
     return t["bytes_per_launch"]
 
@@ -475,7 +503,7 @@ def pmc_summarize(workload, mode, fetch_dir, write_dir):
                      "kernel_kib_avg": sum(kern) / len(kern), "launches": len(kern),
                      "kernel_bytes_avg": factor * sum(kern) / len(kern)}
     res = {"workload": workload, "act_mode": mode, "kernel": dominant_kernel_name(w, mode),
-           "source_hash": source_hash(w.T, mode),
+           "source_hash": source_hash(w, mode),
            "bytes_per_launch": round(out["FETCH_SIZE"]["kernel_bytes_avg"]
                                      + out["WRITE_SIZE"]["kernel_bytes_avg"]),
            "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"]}

@@ -208,12 +208,13 @@ int32_t moe_combine(const float* y_perm, const float* topk_w, const int32_t* pai
  * fp32 [T][E], ids int32 [T][k], weights fp32 [T][k].  The lowering follows
  * the row count (gitee "dgpp" README, "Highlights": row-aware execution):
  * T <= 8 runs the decode lowering (each active expert's weights streamed once
- * for all its tokens), and so does T <= 16 with T*k <= 256 when every
+ * for all its tokens), and so does T <= 32 with T*k <= 512 when every
  * projection has the aligned tile (FP4 gate/up with H a multiple of 2048 and
  * H <= 4096; FP4 or FP8 down projections with I a multiple of 512, I <= 4096
  * and H a multiple of 64; whole-chunk FP4 scale words); otherwise 9..64 rows
- * run the expert GEMV, larger T the grouped GEMM over a tile list.  Errors: MOE_ERR_INVALID_ARG (T < 0, null or misaligned x /
- * out), MOE_ERR_WORKSPACE (ws null, misaligned or below
+ * run the expert GEMV, larger T the grouped GEMM over a tile list.
+ * Errors: MOE_ERR_INVALID_ARG (T < 0, null or misaligned x / out),
+ * MOE_ERR_WORKSPACE (ws null, misaligned or below
  * moe_workspace_size(L, T)), MOE_ERR_UNSUPPORTED (a shape or format the
  * descriptor check rejects), MOE_ERR_HIP (a launch failed; moe_last_error
  * gives the text).  T == 0 returns MOE_OK and launches nothing. */
@@ -320,7 +321,8 @@ int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int
                                  const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                                  void* ws, size_t ws_bytes, int32_t act_mode, void* stream);
 
-/* The decode lowering's gate/up stage alone (T <= 8), on a given routing:
+/* The decode lowering's gate/up stage alone (the rows moe_layer_forward
+ * gives to it: T <= 8, up to 32 on aligned shapes), on a given routing:
  * each active routed expert's gate and up projections streamed once for all
  * of its tokens, both in one pass with SwiGLU in the epilogue (the pages pair
  * gate and up in one launch: gitee "dgpp" README, "Execution and
@@ -329,7 +331,7 @@ int32_t moe_layer_forward_routed(const moe_layer_desc* L, const uint16_t* x, int
  *   h        bf16 [T*k][I]: row t*k+j = bf16(silu(x_t.Wg_e^T) * (x_t.Wu_e^T)),
  *            e = topk_ids[t][j] (rows of skipped pairs are not written);
  *   h_shared bf16 [T][I_shared] (the shared expert), NULL without one.
- * T > 8 returns MOE_ERR_UNSUPPORTED.  This is the first of the decode
+ * Other T returns MOE_ERR_UNSUPPORTED.  This is the first of the decode
  * lowering's expert launches, exposed so that it can be timed and checked on
  * its own; moe_layer_forward runs it wherever it takes the decode lowering. */
 int32_t moe_decode_gate_up(const moe_layer_desc* L, const uint16_t* x, int32_t T,

@@ -1,4 +1,4 @@
-// Decode lowering (T <= 8 rows; up to 16 where every launch has its aligned
+// Decode lowering (T <= 8 rows; up to 32 where every launch has its aligned
 // tile) of the whole layer.
 //
 // Decode is a weight-streaming problem (forum thread "DGPP: a GB10-optimized
@@ -21,7 +21,7 @@
 //   4. one token: per (token, 16 output columns), the down projections of
 //      the token's k slots and of the shared expert, combined in slot order
 //      in fp32 and rounded once to bf16;
-//      2 to 16 tokens: per (expert group, 64 output rows), the down
+//      2 to 32 tokens: per (expert group, 64 output rows), the down
 //      projection once for all of the expert's tokens into fp32 y (pair
 //      order), then
 //   5. the slot-order combine (combine.hip).
@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kRH = 128;  // router rows per slice
 constexpr int kTmax = 8;  // decode rows
-constexpr int kPmax = kTmax * kMaxTopK;
+constexpr int kPmax = 512;  // (token, slot) pairs of a decode call
 constexpr int kRSBatch = 16;
 
 template <int NT>
@@ -187,10 +187,11 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a)
 // Expert group of pair slot q: the expert e = ids[q] and all (token, slot)
 // pairs routed to it, in pair order.  Only the first pair of each expert
 // proceeds (returns false for the others), so every active expert is
-// processed exactly once.  Block-wide, two barriers.
+// processed exactly once.  Block-wide (256 threads), two barriers per 256
+// pair slots.
 struct GroupSmem {
-  int pairs[kPmax];
-  int toks[kPmax];
+  int16_t pairs[kPmax];  // 16 bits keep the block's LDS within two workgroups per CU
+  int16_t toks[kPmax];
   int wcnt[4];
   int wdup[4];
 };
@@ -210,29 +211,60 @@ __device__ inline bool derive_group(const DecodeArgs& a, int q, GroupSmem& g, in
   }
   const int P = a.T * a.k;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // the slot's id and the first round's ids in one round trip
   const int e = a.ids[q];
-  const int j = threadIdx.x;  // P <= 256 = blockDim
-  const int my = (j < P) ? a.ids[j] : -1;
-  const bool m = (j < P) && my == e;
-  const uint64_t bal = __ballot(m);
-  const uint64_t dup = __ballot(m && j < q);
-  if (lane == 0) {
-    g.wcnt[wave] = __popcll(bal);
-    g.wdup[wave] = dup != 0ull;
+  int my = ((int)threadIdx.x < P) ? a.ids[threadIdx.x] : -1;
+  if (P <= kWave * 4) {  // one round (straight-line: 0.5 us less at 8 tokens)
+    const int j = threadIdx.x;
+    const bool m = (j < P) && my == e;
+    const uint64_t bal = __ballot(m);
+    const uint64_t dup = __ballot(m && j < q);
+    if (lane == 0) {
+      g.wcnt[wave] = __popcll(bal);
+      g.wdup[wave] = dup != 0ull;
+    }
+    __syncthreads();
+    if (g.wdup[0] | g.wdup[1] | g.wdup[2] | g.wdup[3]) return false;  // uniform
+    if ((unsigned)e >= (unsigned)a.E) return false;                      // uniform
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += g.wcnt[w];
+    if (m) {
+      const int pos = base + __popcll(bal & lt);
+      g.pairs[pos] = (int16_t)j;
+      g.toks[pos] = (int16_t)(j / a.k);
+    }
+    e_out = e;
+    n_out = g.wcnt[0] + g.wcnt[1] + g.wcnt[2] + g.wcnt[3];
+    __syncthreads();
+    return true;
   }
-  __syncthreads();
-  if (g.wdup[0] | g.wdup[1] | g.wdup[2] | g.wdup[3]) return false;
-  if ((unsigned)e >= (unsigned)a.E) return false;
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += g.wcnt[w];
-  if (m) {
-    const int pos = base + __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-    g.pairs[pos] = j;
-    g.toks[pos] = j / a.k;
+  int n = 0;
+  for (int j0 = 0; j0 < P; j0 += kWave * 4) {
+    const int j = j0 + (int)threadIdx.x;
+    if (j0 > 0) my = (j < P) ? a.ids[j] : -1;
+    const bool m = (j < P) && my == e;
+    const uint64_t bal = __ballot(m);
+    const uint64_t dup = __ballot(m && j < q);
+    if (lane == 0) {
+      g.wcnt[wave] = __popcll(bal);
+      g.wdup[wave] = dup != 0ull;
+    }
+    __syncthreads();
+    if (g.wdup[0] | g.wdup[1] | g.wdup[2] | g.wdup[3]) return false;  // uniform
+    if ((unsigned)e >= (unsigned)a.E) return false;                      // uniform
+    int base = n;
+    for (int w = 0; w < wave; ++w) base += g.wcnt[w];
+    if (m) {
+      const int pos = base + __popcll(bal & lt);
+      g.pairs[pos] = (int16_t)j;
+      g.toks[pos] = (int16_t)(j / a.k);
+    }
+    n += g.wcnt[0] + g.wcnt[1] + g.wcnt[2] + g.wcnt[3];
+    __syncthreads();  // pairs visible; wcnt / wdup free for the next round
   }
   e_out = e;
-  n_out = g.wcnt[0] + g.wcnt[1] + g.wcnt[2] + g.wcnt[3];
-  __syncthreads();
+  n_out = n;
   return true;
 }
 
@@ -244,9 +276,9 @@ constexpr int kGuWK = GemvShape<kOpGateUp>::WK;  // K split of the gate/up tiles
 // per-load bounds test: wavefront w takes the contiguous K quarter
 // [w K/4, (w+1) K/4) in whole batches of four 128-K chunks, every lane's loads of a
 // batch share one base address per matrix (immediate offsets), the group's
-// input rows (at most 16 tokens) are staged once in LDS and read from there
+// input rows (16 at a time) are staged in LDS and read from there
 // as the MFMA B operand, and the four quarters are summed in a fixed order.
-constexpr int kLeanMaxRows = 16;  // the MFMA B operand's 16 columns
+constexpr int kLeanMaxRows = 16;  // rows per chunk: the MFMA B operand's 16 columns
 constexpr int kLeanMaxK = 4096;
 
 struct LeanSmem {
@@ -284,8 +316,8 @@ __device__ __forceinline__ void lean_x_dma(const DecodeArgs& a, LeanSmem& sm) {
 // output rows pairs[] of h).  FP8 (block-128) chunks carry 32 codes per lane
 // in two loads and a block scale applied to each chunk's partial sum.
 template <int FMT, bool XDMA, bool SHARED>
-__device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const int* toks,
-                                    const int* pairs, int tile, LeanSmem& sm) {
+__device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const int16_t* toks,
+                                    const int16_t* pairs, int tile, LeanSmem& sm) {
   static_assert(FMT == FMT_NVFP4 || FMT == FMT_MXFP4 || FMT == FMT_FP8, "lean layouts");
   constexpr bool kFp8 = FMT == FMT_FP8;
   const WDesc& gw = SHARED ? a.sg : a.gate;
@@ -293,20 +325,6 @@ __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const
   const int H = a.H, I = SHARED ? a.I_shared : a.I;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
-  // the group's input rows into LDS by DMA (1 KiB per wavefront
-  // instruction, no register round trip): 8-token layers -0.25 us (NVFP4),
-  // -0.7 us (MXFP4) against 16-byte loads through registers
-  if constexpr (!XDMA) {
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.x), (short)0, a.T * H * 2, 0x00020000);
-    const int ppr = H / (kWave * 8);  // DMA instructions per row
-    for (int ii = wave; ii < nrows * ppr; ii += kGuWK) {
-      const int row = ii / ppr, piece = ii - row * ppr;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (lds_ptr_t)(sm.x + row * H + piece * kWave * 8), 16,
-          2 * ((SHARED ? row : toks[row]) * H + piece * kWave * 8) + 16 * lane, 0, 0, 0);
-    }
-  }
   const int n0 = tile * 16;
   const int rb = kFp8 ? H : H / 2;  // code bytes per row
   constexpr int cbytes = kFp8 ? 128 : 64;  // code bytes per 128-K chunk and row
@@ -322,90 +340,114 @@ __device__ inline void gate_up_lean(const DecodeArgs& a, int e, int nrows, const
     tsg = gw.tscale[e];
     tsu = uw.tscale[e];
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
-  __syncthreads();  // x staged
-  f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
-  const uint16_t* xr = (r < nrows) ? sm.x + r * H : nullptr;
-  // chunks per batch of loads (FP8: two, which keeps the kernel at 104 VGPRs
-  // where four would need 152)
-  constexpr int kB = kFp8 ? 2 : 4;
-  for (int cb = c0; cb < c0 + spw; cb += kB) {
-    ARaw<FMT> pg[kB], pu[kB];
-#pragma unroll
-    for (int d = 0; d < kB; ++d) {
-      if constexpr (kFp8) {
-        pg[d].q0 = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d));
-        pg[d].q1 = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d) + 16);
-        pu[d].q0 = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d));
-        pu[d].q1 = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d) + 16);
-        pg[d].s = reinterpret_cast<const float*>(gs)[cb + d];
-        pu[d].s = reinterpret_cast<const float*>(us)[cb + d];
-      } else {
-        pg[d].q = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d));
-        pu[d].q = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d));
+  // The group's rows in chunks of 16 (the MFMA B operand's columns); the
+  // weights of a chunk after the first come from L2.  The reduction barrier
+  // of a chunk also orders every wavefront's LDS reads of its rows before
+  // the next chunk's DMA overwrites them.
+  for (int c0r = 0; c0r < nrows; c0r += kLeanMaxRows) {
+    const int nr = min(kLeanMaxRows, nrows - c0r);
+    // the group's input rows into LDS by DMA (1 KiB per wavefront
+    // instruction, no register round trip): 8-token layers -0.25 us (NVFP4),
+    // -0.7 us (MXFP4) against 16-byte loads through registers
+    if constexpr (!XDMA) {
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(a.x), (short)0, a.T * H * 2, 0x00020000);
+      const int ppr = H / (kWave * 8);  // DMA instructions per row
+      for (int ii = wave; ii < nr * ppr; ii += kGuWK) {
+        const int row = ii / ppr, piece = ii - row * ppr;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (lds_ptr_t)(sm.x + row * H + piece * kWave * 8), 16,
+            2 * ((SHARED ? c0r + row : toks[c0r + row]) * H + piece * kWave * 8) + 16 * lane, 0, 0,
+            0);
       }
     }
-    if constexpr (!kFp8) {
-      uint2 swg, swu;
-      if constexpr (FMT == FMT_NVFP4) {
-        swg = *reinterpret_cast<const uint2*>(gs + 8 * (cb + g));
-        swu = *reinterpret_cast<const uint2*>(us + 8 * (cb + g));
-      } else {
-        swg = make_uint2(*reinterpret_cast<const uint32_t*>(gs + 4 * (cb + g)), 0u);
-        swu = make_uint2(*reinterpret_cast<const uint32_t*>(us + 4 * (cb + g)), 0u);
-      }
-      const uint2 og = exchange_scales<FMT>(swg, sm.sx[wave][0], r, g);
-      const uint2 ou = exchange_scales<FMT>(swu, sm.sx[wave][1], r, g);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
+    __syncthreads();  // x staged
+    f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
+    const uint16_t* xr = (r < nr) ? sm.x + r * H : nullptr;
+    // chunks per batch of loads (FP8: two, which keeps the kernel at 104 VGPRs
+    // where four would need 152)
+    constexpr int kB = kFp8 ? 2 : 4;
+    for (int cb = c0; cb < c0 + spw; cb += kB) {
+      ARaw<FMT> pg[kB], pu[kB];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        pg[d].s = scale_of_chunk<FMT>(og, d);
-        pu[d].s = scale_of_chunk<FMT>(ou, d);
+      for (int d = 0; d < kB; ++d) {
+        if constexpr (kFp8) {
+          pg[d].q0 = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d));
+          pg[d].q1 = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d) + 16);
+          pu[d].q0 = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d));
+          pu[d].q1 = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d) + 16);
+          pg[d].s = reinterpret_cast<const float*>(gs)[cb + d];
+          pu[d].s = reinterpret_cast<const float*>(us)[cb + d];
+        } else {
+          pg[d].q = *reinterpret_cast<const u32x4*>(gq + cbytes * (cb + d));
+          pu[d].q = *reinterpret_cast<const u32x4*>(uq + cbytes * (cb + d));
+        }
+      }
+      if constexpr (!kFp8) {
+        uint2 swg, swu;
+        if constexpr (FMT == FMT_NVFP4) {
+          swg = *reinterpret_cast<const uint2*>(gs + 8 * (cb + g));
+          swu = *reinterpret_cast<const uint2*>(us + 8 * (cb + g));
+        } else {
+          swg = make_uint2(*reinterpret_cast<const uint32_t*>(gs + 4 * (cb + g)), 0u);
+          swu = make_uint2(*reinterpret_cast<const uint32_t*>(us + 4 * (cb + g)), 0u);
+        }
+        const uint2 og = exchange_scales<FMT>(swg, sm.sx[wave][0], r, g);
+        const uint2 ou = exchange_scales<FMT>(swu, sm.sx[wave][1], r, g);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          pg[d].s = scale_of_chunk<FMT>(og, d);
+          pu[d].s = scale_of_chunk<FMT>(ou, d);
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < kB; ++d) {
+        u32x4 bx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bx[i] = xr ? *reinterpret_cast<const u32x4*>(xr + 128 * (cb + d) + 32 * g + 8 * i)
+                     : u32x4{0, 0, 0, 0};
+        // FP8: each chunk's sum starts from zero and is scaled by its block scale
+        f32x4 tg = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : ag, tu = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : au;
+        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pg[d]), as_bf16x8(bx[0]), tg, 0, 0, 0);
+        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pu[d]), as_bf16x8(bx[0]), tu, 0, 0, 0);
+        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pg[d]), as_bf16x8(bx[1]), tg, 0, 0, 0);
+        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pu[d]), as_bf16x8(bx[1]), tu, 0, 0, 0);
+        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pg[d]), as_bf16x8(bx[2]), tg, 0, 0, 0);
+        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pu[d]), as_bf16x8(bx[2]), tu, 0, 0, 0);
+        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pg[d]), as_bf16x8(bx[3]), tg, 0, 0, 0);
+        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pu[d]), as_bf16x8(bx[3]), tu, 0, 0, 0);
+        if constexpr (kFp8) {
+          ag = ag + pg[d].s * tg;
+          au = au + pu[d].s * tu;
+        } else {
+          ag = tg;
+          au = tu;
+        }
       }
     }
+    // the four K quarters, summed in order
+    sm.red[wave][0][lane] = ag;
+    sm.red[wave][1][lane] = au;
+    __syncthreads();
+    if (wave == 0 && r < nr) {
+      f32x4 sg = sm.red[0][0][lane], su = sm.red[0][1][lane];
 #pragma unroll
-    for (int d = 0; d < kB; ++d) {
-      u32x4 bx[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bx[i] = xr ? *reinterpret_cast<const u32x4*>(xr + 128 * (cb + d) + 32 * g + 8 * i)
-                   : u32x4{0, 0, 0, 0};
-      // FP8: each chunk's sum starts from zero and is scaled by its block scale
-      f32x4 tg = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : ag, tu = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : au;
-      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pg[d]), as_bf16x8(bx[0]), tg, 0, 0, 0);
-      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pu[d]), as_bf16x8(bx[0]), tu, 0, 0, 0);
-      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pg[d]), as_bf16x8(bx[1]), tg, 0, 0, 0);
-      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pu[d]), as_bf16x8(bx[1]), tu, 0, 0, 0);
-      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pg[d]), as_bf16x8(bx[2]), tg, 0, 0, 0);
-      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pu[d]), as_bf16x8(bx[2]), tu, 0, 0, 0);
-      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pg[d]), as_bf16x8(bx[3]), tg, 0, 0, 0);
-      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pu[d]), as_bf16x8(bx[3]), tu, 0, 0, 0);
-      if constexpr (kFp8) {
-        ag = ag + pg[d].s * tg;
-        au = au + pu[d].s * tu;
-      } else {
-        ag = tg;
-        au = tu;
+      for (int w = 1; w < kGuWK; ++w) {
+        sg = sg + sm.red[w][0][lane];
+        su = su + sm.red[w][1][lane];
       }
+      // lane (r, g): rows n0 + 4g + j of group row c0r + r
+      uint16_t hv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hv[j] = f32_to_bf16(silu_fast(sg[j] * tsg) * (su[j] * tsu));
+      uint16_t* o = SHARED ? a.hs + (size_t)(c0r + r) * I + n0 + 4 * g
+                           : a.h + (size_t)pairs[c0r + r] * I + n0 + 4 * g;
+      *reinterpret_cast<uint2*>(o) =
+          make_uint2(hv[0] | (uint32_t(hv[1]) << 16), hv[2] | (uint32_t(hv[3]) << 16));
     }
   }
-  // the four K quarters, summed in order
-  sm.red[wave][0][lane] = ag;
-  sm.red[wave][1][lane] = au;
-  __syncthreads();
-  if (wave != 0 || r >= nrows) return;
-  f32x4 sg = sm.red[0][0][lane], su = sm.red[0][1][lane];
-#pragma unroll
-  for (int w = 1; w < kGuWK; ++w) {
-    sg = sg + sm.red[w][0][lane];
-    su = su + sm.red[w][1][lane];
-  }
-  // lane (r, g): rows n0 + 4g + j of group row r
-  uint16_t hv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) hv[j] = f32_to_bf16(silu_fast(sg[j] * tsg) * (su[j] * tsu));
-  uint16_t* o = SHARED ? a.hs + (size_t)r * I + n0 + 4 * g : a.h + (size_t)pairs[r] * I + n0 + 4 * g;
-  *reinterpret_cast<uint2*>(o) =
-      make_uint2(hv[0] | (uint32_t(hv[1]) << 16), hv[2] | (uint32_t(hv[3]) << 16));
 }
 
 // The shared expert runs the lean tile too when its format has one and its
@@ -470,7 +512,7 @@ __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs
   }
 }
 
-// ---- down projection per expert (2 to 16 tokens) -----------------------------
+// ---- down projection per expert (2 to 32 tokens) -----------------------------
 // A block takes 64 output rows (four wavefronts of 16) of one expert's down
 // projection over all of K = I, for every row of the expert's group (the
 // group's h rows staged in LDS are the MFMA's B operand), so each expert's
@@ -482,6 +524,13 @@ __global__ __launch_bounds__(kWave * kGuWK) void decode_gateup_kernel(DecodeArgs
 // chunk partial.
 constexpr int kDnRows = 16 * kGuWK;  // output rows per block
 
+// Its LDS: the scale exchange and up to 16 h rows (no K reduction across
+// wavefronts, so none of LeanSmem's reduction buffers).
+struct DownSmem {
+  ScaleXchg sx[kGuWK][1];
+  __attribute__((aligned(16))) uint16_t x[kLeanMaxRows * kLeanMaxK];
+};
+
 template <int FMT>
 __host__ __device__ __forceinline__ bool down_lean_fits(const WDesc& w, int K, int H) {
   // whole 512-value DMA pieces per h row; FP4 loads in batches of four chunks
@@ -491,29 +540,14 @@ __host__ __device__ __forceinline__ bool down_lean_fits(const WDesc& w, int K, i
 }
 
 template <int FMT, bool SHARED>
-__device__ inline void down_lean(const DecodeArgs& a, int e, int nrows, const int* pairs, int tile,
-                                 LeanSmem& sm) {
+__device__ inline void down_lean(const DecodeArgs& a, int e, int nrows, const int16_t* pairs, int tile,
+                                 DownSmem& sm) {
   static_assert(FMT == FMT_NVFP4 || FMT == FMT_MXFP4 || FMT == FMT_FP8, "lean layouts");
   constexpr bool kFp8 = FMT == FMT_FP8;
   const WDesc& dw = SHARED ? a.sd : a.down;
   const int K = SHARED ? a.I_shared : a.I, H = a.H;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
-  // the group's h rows into LDS by DMA (1 KiB per wavefront instruction)
-  {
-    const uint16_t* base = SHARED ? a.hs : a.h;
-    const int nsrc = SHARED ? a.T : a.T * a.k;  // rows of the source buffer
-    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(base), (short)0, nsrc * K * 2, 0x00020000);
-    const int ppr = K / (kWave * 8);  // DMA instructions per row
-    for (int ii = wave; ii < nrows * ppr; ii += kGuWK) {
-      const int row = ii / ppr, piece = ii - row * ppr;
-      const int srow = SHARED ? row : pairs[row];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(sm.x + row * K + piece * kWave * 8),
-                                               16, 2 * (srow * K + piece * kWave * 8) + 16 * lane,
-                                               0, 0, 0);
-    }
-  }
   const int n0 = tile * kDnRows + 16 * wave;
   const int rb = kFp8 ? K : K / 2;
   constexpr int cbytes = kFp8 ? 128 : 64;
@@ -522,63 +556,86 @@ __device__ inline void down_lean(const DecodeArgs& a, int e, int nrows, const in
   const uint8_t* ws = scale_row_ptr<FMT>(dw, e, n0 + r);
   float ts = 1.0f;
   if constexpr (FMT == FMT_NVFP4) ts = dw.tscale[e];
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
-  __syncthreads();  // h staged
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* hr = (r < nrows) ? sm.x + r * K : nullptr;
-  constexpr int kB = kFp8 ? 2 : 4;
-  const int nch = K / 128;
-  for (int cb = 0; cb < nch; cb += kB) {
-    ARaw<FMT> pw[kB];
-#pragma unroll
-    for (int d = 0; d < kB; ++d) {
-      if constexpr (kFp8) {
-        pw[d].q0 = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d));
-        pw[d].q1 = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d) + 16);
-        pw[d].s = reinterpret_cast<const float*>(ws)[cb + d];
-      } else {
-        pw[d].q = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d));
+  // The group's rows in chunks of 16 (the MFMA B operand's columns); a
+  // barrier keeps the next chunk's DMA behind every wavefront's reads.
+  for (int c0r = 0; c0r < nrows; c0r += kLeanMaxRows) {
+    const int nr = min(kLeanMaxRows, nrows - c0r);
+    if (c0r > 0) __syncthreads();
+    // the group's h rows into LDS by DMA (1 KiB per wavefront instruction)
+    {
+      const uint16_t* base = SHARED ? a.hs : a.h;
+      const int nsrc = SHARED ? a.T : a.T * a.k;  // rows of the source buffer
+      const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(base), (short)0, nsrc * K * 2, 0x00020000);
+      const int ppr = K / (kWave * 8);  // DMA instructions per row
+      for (int ii = wave; ii < nr * ppr; ii += kGuWK) {
+        const int row = ii / ppr, piece = ii - row * ppr;
+        const int srow = SHARED ? c0r + row : pairs[c0r + row];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(sm.x + row * K + piece * kWave * 8),
+                                                 16, 2 * (srow * K + piece * kWave * 8) + 16 * lane,
+                                                 0, 0, 0);
       }
     }
-    if constexpr (!kFp8) {
-      uint2 sw;
-      if constexpr (FMT == FMT_NVFP4)
-        sw = *reinterpret_cast<const uint2*>(ws + 8 * (cb + g));
-      else
-        sw = make_uint2(*reinterpret_cast<const uint32_t*>(ws + 4 * (cb + g)), 0u);
-      const uint2 o = exchange_scales<FMT>(sw, sm.sx[wave][0], r, g);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA has landed
+    __syncthreads();  // h staged
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* hr = (r < nr) ? sm.x + r * K : nullptr;
+    constexpr int kB = kFp8 ? 2 : 4;
+    const int nch = K / 128;
+    for (int cb = 0; cb < nch; cb += kB) {
+      ARaw<FMT> pw[kB];
 #pragma unroll
-      for (int d = 0; d < kB; ++d) pw[d].s = scale_of_chunk<FMT>(o, d);
+      for (int d = 0; d < kB; ++d) {
+        if constexpr (kFp8) {
+          pw[d].q0 = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d));
+          pw[d].q1 = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d) + 16);
+          pw[d].s = reinterpret_cast<const float*>(ws)[cb + d];
+        } else {
+          pw[d].q = *reinterpret_cast<const u32x4*>(wq + cbytes * (cb + d));
+        }
+      }
+      if constexpr (!kFp8) {
+        uint2 sw;
+        if constexpr (FMT == FMT_NVFP4)
+          sw = *reinterpret_cast<const uint2*>(ws + 8 * (cb + g));
+        else
+          sw = make_uint2(*reinterpret_cast<const uint32_t*>(ws + 4 * (cb + g)), 0u);
+        const uint2 o = exchange_scales<FMT>(sw, sm.sx[wave][0], r, g);
+#pragma unroll
+        for (int d = 0; d < kB; ++d) pw[d].s = scale_of_chunk<FMT>(o, d);
+      }
+#pragma unroll
+      for (int d = 0; d < kB; ++d) {
+        u32x4 bx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bx[i] = hr ? *reinterpret_cast<const u32x4*>(hr + 128 * (cb + d) + 32 * g + 8 * i)
+                     : u32x4{0, 0, 0, 0};
+        f32x4 t = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc;
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pw[d]), as_bf16x8(bx[0]), t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pw[d]), as_bf16x8(bx[1]), t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pw[d]), as_bf16x8(bx[2]), t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pw[d]), as_bf16x8(bx[3]), t, 0, 0, 0);
+        if constexpr (kFp8)
+          acc = acc + pw[d].s * t;
+        else
+          acc = t;
+      }
     }
-#pragma unroll
-    for (int d = 0; d < kB; ++d) {
-      u32x4 bx[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bx[i] = hr ? *reinterpret_cast<const u32x4*>(hr + 128 * (cb + d) + 32 * g + 8 * i)
-                   : u32x4{0, 0, 0, 0};
-      f32x4 t = kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc;
-      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 0>(pw[d]), as_bf16x8(bx[0]), t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 1>(pw[d]), as_bf16x8(bx[1]), t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 2>(pw[d]), as_bf16x8(bx[2]), t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_a<FMT, 3>(pw[d]), as_bf16x8(bx[3]), t, 0, 0, 0);
-      if constexpr (kFp8)
-        acc = acc + pw[d].s * t;
-      else
-        acc = t;
+    if (r < nr) {
+      // lane (r, g): output rows n0 + 4g + j of group row c0r + r
+      float* o = SHARED ? a.ys + (size_t)(c0r + r) * H + n0 + 4 * g
+                        : a.y + (size_t)pairs[c0r + r] * H + n0 + 4 * g;
+      *reinterpret_cast<f32x4*>(o) = acc * ts;
     }
   }
-  if (r >= nrows) return;
-  // lane (r, g): output rows n0 + 4g + j of group row r
-  float* o = SHARED ? a.ys + (size_t)r * H + n0 + 4 * g : a.y + (size_t)pairs[r] * H + n0 + 4 * g;
-  *reinterpret_cast<f32x4*>(o) = acc * ts;
 }
 
 template <int RFMT, int SFMT>
 __global__ __launch_bounds__(kWave * kGuWK) void decode_down_kernel(DecodeArgs a) {
   __shared__ GroupSmem grp;
   extern __shared__ __attribute__((aligned(16))) char lean_dyn[];
-  LeanSmem& lsm = *reinterpret_cast<LeanSmem*>(lean_dyn);
+  DownSmem& lsm = *reinterpret_cast<DownSmem*>(lean_dyn);
   const int ntiles = a.H / kDnRows;
   const int nsd = (SFMT != 0) ? ntiles : 0;
   if ((int)blockIdx.x < nsd) {
@@ -760,8 +817,8 @@ struct GateUpLaunch {
     const int ngu = a.T * a.k * (a.I / gemv_rows_per_block<kOpGateUp>());
     if constexpr ((RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4) && kSharedLean<SFMT>) {
       if (lean_fits(a) && shared_lean_fits<SFMT>(a)) {
-        // the aligned tile's LDS: reductions, scale exchange, T input rows
-        const size_t dyn = offsetof(LeanSmem, x) + (size_t)a.T * a.H * 2;
+        // the aligned tile's LDS: reductions, scale exchange, up to 16 input rows
+        const size_t dyn = offsetof(LeanSmem, x) + (size_t)std::min(a.T, kLeanMaxRows) * a.H * 2;
         return launch(decode_gateup_kernel<RFMT, SFMT, true>, dim3(nsg + ngu), dim3(kWave * kGuWK),
                       dyn, s, a);
       }
@@ -771,7 +828,7 @@ struct GateUpLaunch {
   }
 };
 
-// The per-expert down launch and the combine, for 2 to 16 tokens when the
+// The per-expert down launch and the combine, for 2 to 32 tokens when the
 // down projections have lean tiles and the y buffers are given.
 template <int RFMT, int SFMT>
 constexpr bool kDownLean = (RFMT == FMT_NVFP4 || RFMT == FMT_MXFP4 || RFMT == FMT_FP8) &&
@@ -788,7 +845,7 @@ struct DownLaunch {
         const int ntiles = a.H / kDnRows;
         const int nsd = (SFMT != 0) ? ntiles : 0;
         const int kmax = std::max(a.I, (SFMT != 0) ? a.I_shared : 0);
-        const size_t dyn = offsetof(LeanSmem, x) + (size_t)a.T * kmax * 2;
+        const size_t dyn = offsetof(DownSmem, x) + (size_t)std::min(a.T, kLeanMaxRows) * kmax * 2;
         hipError_t err = launch(decode_down_kernel<RFMT, SFMT>, dim3(nsd + a.T * a.k * ntiles),
                                 dim3(kWave * kGuWK), dyn, s, a);
         if (err != hipSuccess) return err;
@@ -841,10 +898,10 @@ hipError_t by_formats(int rfmt, int sfmt, const DecodeArgs& a, hipStream_t s) {
 
 bool decode_rows_ok(const DecodeArgs& a) {
   if (a.T <= kTmax) return true;
-  // 9..16 rows: only the lean gate/up and the per-expert down, whose groups
-  // fill at most the 16 columns of the MFMA B operand; pair slots <= 256
-  // (one thread per slot in derive_group)
-  if (a.T > kLeanMaxRows || a.T * a.k > kPmax) return false;
+  // 9..32 rows: only the lean gate/up and the per-expert down, which take a
+  // group's rows in chunks of the MFMA B operand's 16 columns; pair slots
+  // <= 512 (two rounds of derive_group)
+  if (a.T > kDecodeMaxRows || a.T * a.k > kPmax) return false;
   if (!(a.gate.fmt == FMT_NVFP4 || a.gate.fmt == FMT_MXFP4) || !lean_fits(a)) return false;
   if (a.has_shared) {
     const int f = a.sg.fmt;
@@ -855,8 +912,7 @@ bool decode_rows_ok(const DecodeArgs& a) {
     if (a.H % kDnRows != 0 || K > kLeanMaxK || K % 512 != 0) return false;
     return ((w.fmt == FMT_NVFP4 || w.fmt == FMT_MXFP4) && w.wide) || w.fmt == FMT_FP8;
   };
-  if (!down_ok(a.down, a.I) || (a.has_shared && !down_ok(a.sd, a.I_shared))) return false;
-  return a.y != nullptr && (!a.has_shared || a.ys != nullptr);
+  return down_ok(a.down, a.I) && (!a.has_shared || down_ok(a.sd, a.I_shared));
 }
 
 DecodePlan decode_plan(int T, int H, int E) {

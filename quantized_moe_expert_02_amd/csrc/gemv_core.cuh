@@ -245,8 +245,8 @@ struct GemvRows {
   int e;                // expert index within the projection
   int p0;               // first output row (permuted position, or 0 for the shared expert)
   int nrows;            // rows in the group
-  const int* rows_in;   // kInList: input row of each group row
-  const int* rows_out;  // kInList: output row of each group row
+  const int16_t* rows_in;   // kInList: input row of each group row
+  const int16_t* rows_out;  // kInList: output row of each group row
 };
 
 // How group row j maps to an input row of `in`.

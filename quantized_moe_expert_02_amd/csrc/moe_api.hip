@@ -155,7 +155,6 @@ struct WsPlan {
   size_t tlog;
 };
 
-constexpr int kDecodeRows = 8;
 
 constexpr int kTileM = kGemmTileM;  // rows per grouped-GEMM tile
 // Calls with at most this many tokens run the expert GEMV lowering: each
@@ -670,7 +669,6 @@ int32_t moe_decode_gate_up(const moe_layer_desc* L, const uint16_t* x, int32_t T
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (!rows_ok(L, T)) return MOE_ERR_UNSUPPORTED;
-  if (T > kDecodeRows) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (x == nullptr || topk_ids == nullptr || h == nullptr || !aligned(x, 16) || !aligned(h, 16) ||
       !aligned(topk_ids, 4))
@@ -678,6 +676,8 @@ int32_t moe_decode_gate_up(const moe_layer_desc* L, const uint16_t* x, int32_t T
   if (L->has_shared && (h_shared == nullptr || !aligned(h_shared, 16))) return MOE_ERR_INVALID_ARG;
   const WsPlan p = plan(L, T);
   DecodeArgs a = decode_args(L, x, T, p);
+  // the rows moe_layer_forward gives to the decode lowering
+  if (T > kDecodeMaxRows || !decode_rows_ok(a)) return MOE_ERR_UNSUPPORTED;
   a.ids = const_cast<int32_t*>(topk_ids);  // only read
   a.h = h;
   a.hs = L->has_shared ? h_shared : nullptr;

@@ -166,9 +166,10 @@ struct DecodeArgs {
   float* ys;          // [T][H] fp32 shared expert's down output, or nullptr
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
-// Rows the decode lowering takes: every T <= 8, and 9..16 when every launch
-// has its aligned (lean) tile for these weights; a.y / a.ys must be set.
-constexpr int kDecodeMaxRows = 16;
+// Rows the decode lowering takes: every T <= 8, and 9..32 (T*k <= 512) when
+// every launch has its aligned (lean) tile for these weights (the layer then
+// sets a.y / a.ys, which the per-expert down needs).
+constexpr int kDecodeMaxRows = 32;
 bool decode_rows_ok(const DecodeArgs& a);
 // Routing alone with the decode router (128-row slices, token groups of 8)
 // and the decode top-k, for batches up to kRouterSlicedRows tokens: reads x,

@@ -81,9 +81,11 @@ def test_layer_decode_full(name):
         f"unique experts={len(np.unique(r['ids']))}")
 
 
-# 9 to 16 rows with the aligned (lean) tiles in every launch: the decode
+# 9 to 32 rows with the aligned (lean) tiles in every launch: the decode
 # lowering (decode router, block top-k, per-group gate/up, per-expert down,
-# combine) with expert groups of up to 16 rows, the MFMA B operand's width.
+# combine); expert groups go through the MFMA B operand's 16 columns in
+# chunks of 16 rows, and more than 256 pair slots take two rounds of the
+# group derivation.
 DECODE_ROWS = {
     # k = E: every group holds all 16 tokens
     "nvfp4_t16_full_groups": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t16_full_groups", T=16,
@@ -101,6 +103,19 @@ DECODE_ROWS = {
                                           T=16, weight_sets=1),
     "decode_t12_mxfp4_zipf": synth.scaled(W["decode_t8_mxfp4_zipf"], name="decode_t12_mxfp4_zipf",
                                           T=12, weight_sets=1),
+    # every group (and the shared expert) in two chunks of 16 rows
+    "nvfp4_t32_full_groups": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t32_full_groups", T=32,
+                                          H=2048, E=4, I=512, top_k=4, I_shared=512,
+                                          shared_fmt=synth.FMT_NVFP4),
+    "mxfp4_t24_k4096": synth.scaled(W["tiny_nvfp4_t4"], name="mxfp4_t24_k4096", T=24, H=4096,
+                                    E=10, I=512, top_k=2, fmt=synth.FMT_MXFP4, I_shared=1024,
+                                    shared_fmt=synth.FMT_FP8, zipf_s=1.1),
+    # 500 pair slots (two derivation rounds), groups of ~17 rows
+    "nvfp4_t25_k20": synth.scaled(W["tiny_nvfp4_t4"], name="nvfp4_t25_k20", T=25, H=2048, E=30,
+                                  I=512, top_k=20, I_shared=512, shared_fmt=synth.FMT_FP8,
+                                  down_fmt=synth.FMT_FP8),
+    "decode_t32_nvfp4_zipf": synth.scaled(W["decode_t32_nvfp4_zipf"], name="decode_t32_nvfp4_zipf",
+                                          weight_sets=1),
 }
 
 
@@ -108,7 +123,8 @@ DECODE_ROWS = {
 def test_layer_decode_rows(name):
     w = DECODE_ROWS[name]
     say(f"[gpu] layer {name}: T={w.T} H={w.H} E={w.E} I={w.I} k={w.top_k} fmt={w.fmt}")
-    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), what=name)
+    tokens = None if w.T <= 16 or w.E <= 64 else [0, 5, 13, 22, 31]
+    r = check_layer_against_oracle(layer_for(w), synth.make_x(w), tokens=tokens, what=name)
     counts = np.bincount(r["ids"].reshape(-1), minlength=w.E)
     say(f"[gpu] layer {name}: rel={r['rel']:.2e} worst={r['worst']:.2e} max group={counts.max()}")
     if w.top_k == w.E:
@@ -497,6 +513,37 @@ def test_decode_gate_up_unit(name):
     assert_close(O.bf16_value(bf16_bits(h)), ref.h.reshape(T * k, I), name + " decode h")
     if L.has_shared:
         assert_close(O.bf16_value(bf16_bits(hs)), ref.h_shared, name + " decode shared h")
+
+
+@pytest.mark.parametrize("name", ["nvfp4_t32_full_groups", "mxfp4_t24_k4096"])
+def test_decode_gate_up_unit_rows(name):
+    """moe_decode_gate_up at 24 and 32 rows on aligned shapes (groups taken
+    in chunks of 16 rows), and MOE_ERR_UNSUPPORTED at 12 rows of a shape whose
+    layer runs the expert GEMV instead."""
+    w = DECODE_ROWS[name]
+    L = layer_for(w)
+    x_bits = synth.make_x(w)
+    T, k, I = w.T, w.top_k, w.I
+    say(f"[gpu] decode gate/up unit {name}: T={T} H={w.H} I={I} k={k} fmt={w.fmt}")
+    ref = O.layer_forward(L, x_bits)
+    dl = device_layer(L)
+    ids = torch.from_numpy(ref.routing.ids).cuda()
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
+    hs = torch.empty((T, w.I_shared), dtype=torch.bfloat16, device="cuda") if L.has_shared else None
+    moe.moe_decode_gate_up(dl.desc, bf16_tensor(x_bits), T, ids, h, hs)
+    torch.cuda.synchronize()
+    assert_close(O.bf16_value(bf16_bits(h)), ref.h.reshape(T * k, I), name + " decode h")
+    if L.has_shared:
+        assert_close(O.bf16_value(bf16_bits(hs)), ref.h_shared, name + " decode shared h")
+    ws_ = SMALL["nvfp4_t12"]
+    L12 = layer_for(ws_)
+    dl12 = device_layer(L12)
+    x12 = bf16_tensor(synth.make_x(ws_))
+    ids12 = torch.zeros((ws_.T, ws_.top_k), dtype=torch.int32, device="cuda")
+    h12 = torch.empty((ws_.T * ws_.top_k, ws_.I), dtype=torch.bfloat16, device="cuda")
+    hs12 = torch.empty((ws_.T, ws_.I_shared), dtype=torch.bfloat16, device="cuda")
+    st = moe.moe_decode_gate_up(dl12.desc, x12, ws_.T, ids12, h12, hs12, check=False)
+    assert st == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_reuse_across_batch_sizes():

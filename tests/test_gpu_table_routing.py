@@ -87,12 +87,13 @@ def test_layer_on_table_routing(T):
     check_table_routed_layer(w, T)
 
 
-@pytest.mark.parametrize("T", [6, 13])
+@pytest.mark.parametrize("T", [6, 13, 29])
 def test_aligned_layer_on_table_routing(T):
     """The same at a shape with aligned tiles in every decode launch (K a
     multiple of 2048 for gate/up and of 512 for down): the per-expert down
-    projection zero-fills the rows of out-of-range slots, for up to 16 rows."""
-    w = synth.scaled(W["tiny_nvfp4_t4"], name="tab_aligned", T=16, H=2048, E=12, I=512, top_k=3,
+    projection zero-fills the rows of out-of-range slots, for up to 32 rows
+    (groups in chunks of 16)."""
+    w = synth.scaled(W["tiny_nvfp4_t4"], name="tab_aligned", T=32, H=2048, E=12, I=512, top_k=3,
                      I_shared=512, shared_fmt=synth.FMT_NVFP4)
     check_table_routed_layer(w, T)
 
