@@ -48,7 +48,9 @@ struct RouterSmem {
 
 // NT: tokens per block (1 for a single token, else groups of 8), so that a
 // single-token call carries no per-token guards in its unrolled loops.
-template <int NT>
+// PT: the slice sums' type in memory (float up to 8 tokens, double above:
+// see decode_topk_kernel).
+template <int NT, typename PT>
 __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
   __shared__ RouterSmem<NT> sm;
   const int rb = blockIdx.x;
@@ -110,11 +112,12 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
       s += sm.red[g][t][col];
       av += sm.reda[g][t][col];
     }
-    a.part[((size_t)rs * T + t0 + t) * E + e] = static_cast<float>(s);
+    reinterpret_cast<PT*>(a.part)[((size_t)rs * T + t0 + t) * E + e] = static_cast<PT>(s);
     a.apart[((size_t)rs * T + t0 + t) * E + e] = av;
   }
 }
 
+template <typename PT>
 __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a) {
   __shared__ double v[kMaxExperts];
   __shared__ WaveTopkScratch wsc;
@@ -126,11 +129,12 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a)
     double l = 0.0;
     float av = 0.f;
     for (int r0 = 0; r0 < a.RS; r0 += kRSBatch) {
-      float pv[kRSBatch], qv[kRSBatch];
+      PT pv[kRSBatch];
+      float qv[kRSBatch];
 #pragma unroll
       for (int j = 0; j < kRSBatch; ++j) {  // unconditional loads: one round trip per batch
         const int r = min(r0 + j, a.RS - 1);
-        pv[j] = a.part[((size_t)r * T + t) * E + e];
+        pv[j] = reinterpret_cast<const PT*>(a.part)[((size_t)r * T + t) * E + e];
         qv[j] = a.apart[((size_t)r * T + t) * E + e];
       }
 #pragma unroll
@@ -155,8 +159,17 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(DecodeArgs a)
   __syncthreads();
   float am = 0.f;
   for (int i = 0; i < (int)(blockDim.x / kWave); ++i) am = fmaxf(am, amax_w[i]);
-  // fast-logit error < 2^-23 * sum|x||w| (covers the fp32 slice roundings)
-  const double bound = static_cast<double>(am) * 0x1p-23;
+  // Fast-logit error.  float64 slice sums (128 exact products: 16 fused
+  // multiply-adds per thread, then eight partial sums; the RS <= 512 slice
+  // additions and the bias in float64 too): at most (16 + 8 + RS + 1) u
+  // sum|x||w| (u = 2^-53) < 2^-43 sum|x||w|.  fp32 slice sums add their
+  // roundings: < 2^-23 sum|x||w|.  am, the same sum in fp32 (positive
+  // terms), is short of it by far less than a factor 2.  With the fp32
+  // bound a top-k gap that close needs the recompute (~11 us on one
+  // wavefront) on about one token in 64, which a batch of 16 or more
+  // tokens nearly always waits for; below 9 tokens the float64 sums' extra
+  // bytes cost more (0.5 us) than the rare recompute.
+  const double bound = static_cast<double>(am) * (sizeof(PT) == 8 ? 0x1p-40 : 0x1p-23);
   // The whole block selects and certifies; only when that fails (close
   // gaps, non-finite values, many ties) does one wavefront recompute what
   // it must.
@@ -925,15 +938,23 @@ DecodePlan decode_plan(int T, int H, int E) {
 }
 
 hipError_t launch_decode_router(const DecodeArgs& a, hipStream_t s) {
-  if (a.T == 1) return launch(decode_router_kernel<1>, dim3(a.RS * a.CS), dim3(256), 0, s, a);
+  if (a.T == 1)
+    return launch(decode_router_kernel<1, float>, dim3(a.RS * a.CS), dim3(256), 0, s, a);
   const dim3 grid(a.RS * a.CS, (a.T + kTmax - 1) / kTmax);
-  return launch(decode_router_kernel<kTmax>, grid, dim3(256), 0, s, a);
+  if (a.T <= kTmax) return launch(decode_router_kernel<kTmax, float>, grid, dim3(256), 0, s, a);
+  return launch(decode_router_kernel<kTmax, double>, grid, dim3(256), 0, s, a);
+}
+
+// The top-k on the slice sums the router wrote (fp32 up to 8 tokens).
+hipError_t launch_decode_topk(const DecodeArgs& a, hipStream_t s) {
+  if (a.T <= kTmax) return launch(decode_topk_kernel<float>, dim3(a.T), dim3(kTopkThreads), 0, s, a);
+  return launch(decode_topk_kernel<double>, dim3(a.T), dim3(kTopkThreads), 0, s, a);
 }
 
 hipError_t launch_decode_route(const DecodeArgs& a, hipStream_t s) {
   hipError_t err = launch_decode_router(a, s);
   if (err != hipSuccess) return err;
-  return launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
+  return launch_decode_topk(a, s);
 }
 
 hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s) {
@@ -949,7 +970,7 @@ hipError_t launch_decode_experts(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   hipError_t err = launch_decode_router(a, s);
   if (err != hipSuccess) return err;
-  err = launch(decode_topk_kernel, dim3(a.T), dim3(kTopkThreads), 0, s, a);
+  err = launch_decode_topk(a, s);
   if (err != hipSuccess) return err;
   err = by_formats<GateUpLaunch>(a.gate.fmt, a.has_shared ? a.sg.fmt : 0, a, s);
   if (err != hipSuccess) return err;

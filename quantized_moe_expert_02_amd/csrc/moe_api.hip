@@ -221,7 +221,7 @@ WsPlan plan(const moe_layer_desc* L, int T) {
   }
   p.dpart = p.dapart = 0;
   if (T <= kRouterSlicedRows) {  // decode router slices (fused decode and the sliced router)
-    p.dpart = take((size_t)p.dp.RS * T * E * 4);
+    p.dpart = take((size_t)p.dp.RS * T * E * 8);
     p.dapart = take((size_t)p.dp.RS * T * E * 4);
   }
   p.tlog = take((size_t)T * E * 4);  // router logits for token-table routing
@@ -285,7 +285,7 @@ int32_t run_route(const moe_layer_desc* L, const uint16_t* x, float* logits, int
     d.bias = L->router_bias;
     d.RS = p.dp.RS;
     d.CS = p.dp.CS;
-    d.part = at<float>(ws, p.dpart);
+    d.part = at<double>(ws, p.dpart);
     d.apart = at<float>(ws, p.dapart);
     d.logits_out = logits;
     d.ids = ids;
@@ -471,7 +471,7 @@ int32_t layer_impl(const moe_layer_desc* L, const uint16_t* x, int32_t T, uint16
   float* w = routed ? const_cast<float*>(given_w) : (dbg_w ? dbg_w : at<float>(ws, p.w));
   if (T <= kDecodeMaxRows) {
     DecodeArgs a = decode_args(L, x, T, p);
-    a.part = at<float>(ws, p.dpart);
+    a.part = at<double>(ws, p.dpart);
     a.apart = at<float>(ws, p.dapart);
     a.logits_out = dbg_logits;
     a.ids = ids;

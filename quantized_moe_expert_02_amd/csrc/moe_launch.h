@@ -153,7 +153,7 @@ struct DecodeArgs {
   WDesc gate, up, down, sg, su, sd;
   int RS, CS;
   // workspace
-  float* part;        // [RS][T][E] fp32 slice sums of x.Wr
+  double* part;       // [RS][T][E] slice sums of x.Wr: fp32 (T <= 8) or fp64 (T > 8)
   float* apart;       // [RS][T][E] fp32 slice sums of |x||Wr|
   float* logits_out;  // [T][E] debug copy or nullptr
   int* ids;           // [T][k]
