@@ -186,7 +186,7 @@ def main():
     log(f"[bench] routing matches the oracle: {routing_exact}")
 
     if args.pmc_probe:
-        pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws, mode_code if lossy else 0)
+        pmc_probe(moe, torch, dev, L, w, sets, nsets, x, ids, ws, mode_code if lossy else 0)
         return
 
     # graph of one pass over the weight sets
@@ -386,7 +386,7 @@ PMC_COPIES = 4
 PMC_LAUNCHES = 8
 
 
-def pmc_probe(moe, torch, dev, L, sets, nsets, x, ids, ws, mode_code):
+def pmc_probe(moe, torch, dev, L, w, sets, nsets, x, ids, ws, mode_code):
     """Dispatches for a counter run: PMC_COPIES plain copies of PMC_COPY_BYTES
     (x * 1 into another buffer; the calibration: bytes per counted KiB), then
     PMC_LAUNCHES launches of
