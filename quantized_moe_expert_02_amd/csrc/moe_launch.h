@@ -139,7 +139,7 @@ hipError_t launch_grouped_gemm_q(int mode, int op, const WDesc& w0, const WDesc&
                                  int max_tiles, const uint8_t* in_codes, const void* in_scales,
                                  void* out, hipStream_t s);
 
-// ---- fused decode lowering (T <= 8) -----------------------------------------
+// ---- fused decode lowering (T <= 8; up to 32 on aligned shapes) -------------
 struct DecodePlan {
   int RS, CS, down_tiles;
 };
