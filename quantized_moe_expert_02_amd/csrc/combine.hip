@@ -10,6 +10,9 @@
 namespace moe {
 namespace {
 
+// PAIR: y rows in pair order (row t*k+j, the decode lowering): the rows'
+// addresses need no load, so the weights and y go out in one round trip.
+template <bool PAIR>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ w,
                                                       const int* __restrict__ p2p,
@@ -33,7 +36,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       pp[b] = -1;
       wj[b] = 0.f;
       if (j0 + b < k) {  // wave-uniform
-        pp[b] = p2p ? p2p[(size_t)t * k + j0 + b] : t * k + j0 + b;
+        pp[b] = PAIR ? t * k + j0 + b : p2p[(size_t)t * k + j0 + b];
         wj[b] = w[(size_t)t * k + j0 + b];
       }
     }
@@ -65,7 +68,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* y, const float* w, const int* pair_to_perm, const float* ys,
                           int T, int k, int H, uint16_t* out, hipStream_t s) {
   dim3 grid((H / 4 + 255) / 256, T);
-  return launch(combine_kernel, grid, dim3(256), 0, s, y, w, pair_to_perm, ys, T, k, H, out);
+  if (pair_to_perm == nullptr)
+    return launch(combine_kernel<true>, grid, dim3(256), 0, s, y, w, pair_to_perm, ys, T, k, H, out);
+  return launch(combine_kernel<false>, grid, dim3(256), 0, s, y, w, pair_to_perm, ys, T, k, H, out);
 }
 
 }  // namespace moe
